@@ -1,0 +1,165 @@
+"""Python binding of libdg.so, the MI355X (gfx950) FP8 block-scaled GEMM library.
+
+Argument marshalling only: every call checks dtypes, devices, shapes and contiguity,
+then passes raw device pointers and torch's current HIP stream to the C ABI declared
+in ``include/dg.h``. All arithmetic runs in the library's HIP kernels; there is no
+fallback path. If libdg.so is missing the import fails.
+
+Calls (DeepGEMM project page, aiproducthub.cn, "quick start"; DeepGEMM launch
+article, deepseek.csdn.net, section 4.2 "advanced tuning"):
+
+* ``fp8_gemm_nt(a, b, c, a_sf, b_sf)``
+* ``m_grouped_fp8_gemm_nt_contiguous(a, b, c, a_sf, b_sf, m_indices)``
+* ``m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None)``
+
+Operands: ``a``/``b`` are ``torch.float8_e4m3fn`` (``torch.uint8`` holding e4m3fn
+codes is accepted too), ``a_sf``/``b_sf`` ``torch.float32``, ``c`` ``torch.bfloat16``
+and the index tensors ``torch.int32``, all on the same GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first: the library then binds to torch's HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdg.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m fp8_block_scaled_dg_amd.build` (hipcc, gfx950)")
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+lib = ctypes.CDLL(LIB_PATH)
+lib.dg_fp8_gemm_nt.restype = ctypes.c_int
+lib.dg_fp8_gemm_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+lib.dg_m_grouped_fp8_gemm_nt_contiguous.restype = ctypes.c_int
+lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                                    _i64, _i32, _vp]
+lib.dg_m_grouped_fp8_gemm_nt_masked.restype = ctypes.c_int
+lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64,
+                                                _i64, _i64, _vp]
+lib.dg_status_string.restype = ctypes.c_char_p
+lib.dg_status_string.argtypes = [ctypes.c_int]
+lib.dg_last_error_detail.restype = ctypes.c_char_p
+lib.dg_last_error_detail.argtypes = []
+lib.dg_describe_config.restype = ctypes.c_int
+lib.dg_describe_config.argtypes = [_i32, _i64, _i64, _i64, _i32, _i64, ctypes.c_char_p, _i64]
+
+KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED = 0, 1, 2
+BLOCK = 128
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        name = lib.dg_status_string(status).decode()
+        detail = lib.dg_last_error_detail().decode()
+        super().__init__(f"{name}: {detail}" if detail else name)
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise DGError(status)
+
+
+def _fp8(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"{name} must be torch.float8_e4m3fn (or uint8 codes), got {t.dtype}")
+    return t
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _dev(t, name, device)
+
+
+def _dev(t: torch.Tensor, name: str, device) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fp8_gemm_nt(a, b, c, a_sf, b_sf) -> None:
+    """c[M][N] (bf16) = block-scaled a[M][K] x b[N][K]^T; writes c in place."""
+    _fp8(a, "a"), _fp8(b, "b")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    M, K = a.shape
+    N = b.shape[0]
+    dev = a.device
+    _dev(a, "a", dev)
+    _need(b, "b", b.dtype, (N, K), dev)
+    _need(c, "c", torch.bfloat16, (M, N), dev)
+    _need(a_sf, "a_sf", torch.float32, (M, K // BLOCK), dev)
+    _need(b_sf, "b_sf", torch.float32, ((N + BLOCK - 1) // BLOCK, K // BLOCK), dev)
+    with torch.cuda.device(dev):
+        check(lib.dg_fp8_gemm_nt(a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(),
+                                 b_sf.data_ptr(), M, N, K, _stream(dev)))
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a, b, c, a_sf, b_sf, m_indices) -> None:
+    """Contiguous MoE layout: row r of a uses expert m_indices[r]'s b (-1 = pad row,
+    left untouched in c)."""
+    _fp8(a, "a"), _fp8(b, "b")
+    if a.dim() != 2 or b.dim() != 3:
+        raise ValueError("a must be [M_total, K] and b [G, N, K]")
+    M, K = a.shape
+    G, N = b.shape[0], b.shape[1]
+    dev = a.device
+    _dev(a, "a", dev)
+    _need(b, "b", b.dtype, (G, N, K), dev)
+    _need(c, "c", torch.bfloat16, (M, N), dev)
+    _need(a_sf, "a_sf", torch.float32, (M, K // BLOCK), dev)
+    _need(b_sf, "b_sf", torch.float32, (G, (N + BLOCK - 1) // BLOCK, K // BLOCK), dev)
+    _need(m_indices, "m_indices", torch.int32, (M,), dev)
+    with torch.cuda.device(dev):
+        check(lib.dg_m_grouped_fp8_gemm_nt_contiguous(
+            a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
+            m_indices.data_ptr(), M, N, K, G, _stream(dev)))
+
+
+def m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None) -> None:
+    """Masked MoE layout: expert e computes its first masked_m[e] rows of a[e]; the
+    other rows of c[e] are left untouched."""
+    _fp8(a, "a"), _fp8(b, "b")
+    if a.dim() != 3 or b.dim() != 3:
+        raise ValueError("a must be [G, M_max, K] and b [G, N, K]")
+    G, M_max, K = a.shape
+    N = b.shape[1]
+    dev = a.device
+    _dev(a, "a", dev)
+    _need(b, "b", b.dtype, (G, N, K), dev)
+    _need(c, "c", torch.bfloat16, (G, M_max, N), dev)
+    _need(a_sf, "a_sf", torch.float32, (G, M_max, K // BLOCK), dev)
+    _need(b_sf, "b_sf", torch.float32, (G, (N + BLOCK - 1) // BLOCK, K // BLOCK), dev)
+    _need(masked_m, "masked_m", torch.int32, (G,), dev)
+    em = int(expected_m) if expected_m is not None else 0
+    with torch.cuda.device(dev):
+        check(lib.dg_m_grouped_fp8_gemm_nt_masked(
+            a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
+            masked_m.data_ptr(), G, M_max, N, K, em, _stream(dev)))
+
+
+def describe_config(kind: int, M: int, N: int, K: int, G: int = 1, expected_m: int = 0) -> str:
+    buf = ctypes.create_string_buffer(128)
+    check(lib.dg_describe_config(kind, M, N, K, G, expected_m, buf, 128))
+    return buf.value.decode()
+
+
+__all__ = ["fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+           "describe_config", "DGError", "lib", "LIB_PATH"]

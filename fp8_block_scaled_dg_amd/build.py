@@ -1,0 +1,41 @@
+"""Builds libdg.so (the HIP library) in-tree for gfx950 with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB_PATH = os.path.join(PKG, "libdg.so")
+SOURCES = [os.path.join(CSRC, "dg_api.hip")]
+DEPS = SOURCES + [os.path.join(CSRC, "gemm_kernel.hpp"), os.path.join(ROOT, "include", "dg.h")]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+    # no packed-fp32 VALU instructions (v_pk_*_f32) in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def command(out: str = LIB_PATH, extra: list[str] | None = None) -> list[str]:
+    return ["hipcc", *HIPCC_FLAGS, *(extra or []), "-o", out, *SOURCES]
+
+
+def build(verbose: bool = False) -> str:
+    cmd = command()
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError("hipcc failed building libdg.so")
+    if verbose and msgs:
+        sys.stderr.write("\n".join(msgs) + "\n")
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,129 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) FP8 block-scaled GEMM library (libdg.so).
+ *
+ * The operation: an FP8 GEMM where every operand block carries its own fp32
+ * scaling factor and the FP8 products are promoted to FP32 for a second-level
+ * accumulation across K-blocks (DeepGEMM launch article, deepseek.csdn.net,
+ * section 1.2 "precision safeguards"). In the library's layouts:
+ *
+ *     C[m][n] = bf16_rne( sum_{kb < K/128} sfA[m][kb] * sfB[n/128][kb]
+ *                         * sum_{k in [128kb, 128kb+128)} a(m,k) * b(n,k) )
+ *
+ * with a(), b() the values of OCP e4m3fn codes (max 448, no infinities).
+ * Granularity: A is scaled per 1x128 (row, K-block), B per 128x128 block; K-block
+ * 128 for both. The call shape follows the DeepGEMM project page (aiproducthub.cn),
+ * "quick start": fp8_gemm_nt(a, b, c, a_sf, b_sf) and
+ * m_grouped_fp8_gemm_nt_contiguous(...), the caller passing the output buffer. The
+ * masked grouped form is the MoE interface of the launch article's section 4.2
+ * "advanced tuning" (also the library news page, youleyou.com, "performance").
+ *
+ * Conventions shared by every call
+ *  - Every pointer is DEVICE memory owned by the caller; the library never
+ *    allocates, frees or keeps a user buffer. All matrices are row-major and
+ *    dense (leading dimension = row length).
+ *  - A and B hold e4m3fn codes (1 byte). "NT": both are K-contiguous, B is [N][K].
+ *  - C is bf16 (2 bytes), written with one round-to-nearest-even from the fp32
+ *    accumulator. Only the output rows the call produces are written.
+ *  - sfA, sfB are fp32. Any finite positive value works; with powers of two (the
+ *    configured workloads) every scaling step is exact.
+ *  - K % 128 == 0 (K > 0 when any output is produced), N % 16 == 0.
+ *    A, B, C must be 16-byte aligned, sfA and sfB 4-byte aligned.
+ *  - hip_stream is a hipStream_t (NULL = the default stream). The call only
+ *    enqueues work and returns; device faults surface at the caller's next
+ *    synchronisation. Calls on one stream run in order.
+ *  - Results are bitwise deterministic for a given shape (no atomics touch C).
+ *  - Errors: every argument check runs on the host before any HIP call and returns
+ *    a status without touching the GPU; nothing is thrown across the ABI. A
+ *    launch failure returns DG_ERR_LAUNCH. dg_last_error_detail() gives a
+ *    thread-local message for the last failing call on the calling thread.
+ *  - Zero-sized work (M, N or G*M_max == 0) returns DG_OK and launches nothing.
+ *  - Environment: DG_PRINT_CONFIGS=1 prints the tile configuration chosen for each
+ *    new (kind, shape) to stderr.
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dg_status {
+  DG_OK = 0,
+  DG_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                    */
+  DG_ERR_BAD_SHAPE = 2,         /* negative size, K % 128 != 0, N % 16 != 0, G<1 */
+  DG_ERR_UNSUPPORTED_SHAPE = 3, /* valid but beyond what the kernels index       */
+  DG_ERR_MISALIGNED = 4,        /* A/B/C not 16-byte or scales not 4-byte aligned */
+  DG_ERR_NO_DEVICE = 5,         /* no usable gfx950 device                       */
+  DG_ERR_LAUNCH = 6             /* the kernel launch itself failed               */
+} dg_status;
+
+/*
+ * Dense NT GEMM (project page, "quick start": fp8_gemm_nt).
+ *   A   e4m3fn [M][K]            sfA fp32 [M][K/128]
+ *   B   e4m3fn [N][K]            sfB fp32 [ceil(N/128)][K/128]
+ *   C   bf16   [M][N]            every element written
+ */
+dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA,
+                         const float* sfB, int64_t M, int64_t N, int64_t K,
+                         void* hip_stream);
+
+/*
+ * MoE grouped GEMM, contiguous layout (project page, "technical implementation":
+ * several experts' token rows concatenated along M, N and K shared).
+ *   A   e4m3fn [M_total][K]      sfA fp32 [M_total][K/128]
+ *   B   e4m3fn [G][N][K]         sfB fp32 [G][ceil(N/128)][K/128]
+ *   C   bf16   [M_total][N]
+ *   m_indices int32 [M_total] (device): row r is multiplied by expert
+ *   m_indices[r]'s B. A value outside [0, G) -- the pad marker is -1 -- marks a row
+ *   that is neither read into any output nor written: C keeps its bytes there.
+ * Performance contract: each expert's rows form one segment whose start is a
+ * multiple of 128 (pad rows fill the gap). Any m_indices gives correct results;
+ * 128-row groups that mix experts only cost extra passes.
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const void* B, void* C,
+                                              const float* sfA, const float* sfB,
+                                              const int32_t* m_indices, int64_t M_total,
+                                              int64_t N, int64_t K, int32_t G,
+                                              void* hip_stream);
+
+/*
+ * MoE grouped GEMM, masked layout (launch article section 4.2; news page,
+ * "performance"): each expert owns a fixed-capacity slab of M_max rows, of which
+ * the first masked_m[e] are valid.
+ *   A   e4m3fn [G][M_max][K]     sfA fp32 [G][M_max][K/128]
+ *   B   e4m3fn [G][N][K]         sfB fp32 [G][ceil(N/128)][K/128]
+ *   C   bf16   [G][M_max][N]
+ *   masked_m int32 [G] (device), read on the device (no host sync); a value
+ *   outside [0, M_max] is clamped into it. Rows m >= masked_m[e] are neither read
+ *   nor written.
+ *   expected_m: host-side hint of the typical masked_m, used only to pick a tile
+ *   configuration (<= 0 means M_max). It never changes the result.
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
+                                          const float* sfA, const float* sfB,
+                                          const int32_t* masked_m, int32_t G,
+                                          int64_t M_max, int64_t N, int64_t K,
+                                          int64_t expected_m, void* hip_stream);
+
+/* Static string naming a status. */
+const char* dg_status_string(dg_status s);
+
+/* Thread-local description of the last failing call on this thread ("" if none). */
+const char* dg_last_error_detail(void);
+
+/*
+ * Describe the tile configuration a call with these arguments would use, as a
+ * NUL-terminated string written to buf (at most len bytes). kind: 0 dense,
+ * 1 contiguous, 2 masked; for dense pass G = 1, for masked pass M = M_max and
+ * expected_m. Host only; returns DG_ERR_BAD_SHAPE for kinds it does not know.
+ */
+dg_status dg_describe_config(int32_t kind, int64_t M, int64_t N, int64_t K, int32_t G,
+                             int64_t expected_m, char* buf, int64_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H_ */

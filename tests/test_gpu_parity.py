@@ -1,0 +1,316 @@
+"""GPU parity: the HIP library (through its C ABI, via the binding) against the CPU
+oracle, element by element on the same seeded inputs.
+
+* small shapes and edge shapes: every output compared;
+* integer-exact inputs (codes decoding to small integers, power-of-two scales):
+  every block partial and every accumulation step is exact in fp32, so the GPU must
+  equal the oracle's bf16 rounding bitwise -- this pins all indexing;
+* the full workload shapes, in the launch configuration the benchmark times:
+  every output where the oracle is fast enough, sampled outputs (all tile and
+  scale-block boundaries plus seeded random positions) where it is not;
+* rows a grouped call must not produce keep their seeded sentinel bytes, and 64 KB
+  guard bands around every output stay intact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import gpu_util as gu
+from tests.parity import assert_bitwise, assert_parity, report
+
+pytestmark = pytest.mark.gpu
+
+INT_CODES = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50,  # 0,1,2,3,4,5,6,7,8
+                      0xB8, 0xC0, 0xC4, 0xC8, 0xCA, 0xCC, 0xCE, 0xD0], dtype=np.uint8)
+
+
+def dg():
+    import fp8_block_scaled_dg_amd as m
+    return m
+
+
+def int_operands(rng, M, N, K, G=None):
+    KB, NB = K // 128, (N + 127) // 128
+    shape_b = (N, K) if G is None else (G, N, K)
+    A = rng.choice(INT_CODES, size=(M, K))
+    B = rng.choice(INT_CODES, size=shape_b)
+    sfA = np.ldexp(1.0, rng.integers(-2, 3, size=(M, KB))).astype(np.float32)
+    sfB = np.ldexp(1.0, rng.integers(-2, 3, size=(NB, KB) if G is None else (G, NB, KB)))
+    return A.astype(np.uint8), B.astype(np.uint8), sfA, sfB.astype(np.float32)
+
+
+def run_dense(A, B, sfA, sfB, seed=1):
+    M, K = A.shape
+    N = B.shape[0]
+    out = gu.Guarded((M, N), seed)
+    gu.announce(f"dense M={M} N={N} K={K}")
+    dg().fp8_gemm_nt(gu.codes(A), gu.codes(B), out.out, gu.dev(sfA), gu.dev(sfB))
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside C"
+    return out.result()
+
+
+def sample_positions(rng, M, N, n_random=4000, tile=(64, 128)):
+    rows = set([0, M - 1])
+    for t in tile:
+        for b in range(0, M, t):
+            rows.update([b, b - 1, b + 1])
+    cols = set([0, N - 1])
+    for b in range(0, N, 16):
+        if b % 128 == 0 or b % 64 == 0:
+            cols.update([b, b - 1, b + 15, b + 16])
+    rows = np.array(sorted(r for r in rows if 0 <= r < M))
+    cols = np.array(sorted(c for c in cols if 0 <= c < N))
+    # every boundary row against a spread of columns, every boundary column
+    # against a spread of rows, plus random positions
+    rr = [np.repeat(rows, 16), rng.integers(0, M, cols.size * 8), rng.integers(0, M, n_random)]
+    cc = [rng.integers(0, N, rows.size * 16), np.repeat(cols, 8), rng.integers(0, N, n_random)]
+    return np.concatenate(rr).astype(np.int64), np.concatenate(cc).astype(np.int64)
+
+
+# ------------------------------------------------------------------ dense
+
+
+def test_dense_small_workload_full():
+    w = synth.workload("small")
+    g = run_dense(w.A, w.B, w.sfA, w.sfB)
+    r = oracle.gemm_nt(w.A, w.B, w.sfA, w.sfB)
+    rep = assert_parity(g, r, what="small")
+    print("small:", rep)
+    assert rep["bitwise_match"] > 0.98
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (63, 64, 256), (64, 2112, 128), (65, 144, 384),
+                                   (129, 272, 256), (200, 384, 512), (257, 128, 1024),
+                                   (128, 256, 512)])
+def test_dense_integer_exact_bitwise(M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    A, B, sfA, sfB = int_operands(rng, M, N, K)
+    g = run_dense(A, B, sfA, sfB)
+    assert_bitwise(g, oracle.gemm_nt(A, B, sfA, sfB), what=f"int {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 2112, 1024), (300, 528, 640), (1, 32, 128), (17, 4096, 256)])
+def test_dense_gaussian_shapes(M, N, K):
+    w = synth.dense(M, N, K, seed_base=777000 + M)
+    g = run_dense(w.A, w.B, w.sfA, w.sfB)
+    rep = assert_parity(g, oracle.gemm_nt(w.A, w.B, w.sfA, w.sfB), what=f"{M}x{N}x{K}")
+    print(f"{M}x{N}x{K}:", rep)
+
+
+def test_dense_one_hot_identity_doubling_bitwise():
+    rng = np.random.default_rng(5)
+    M, N, K = 96, 384, 384
+    w = synth.dense(M, N, K, seed_base=555000)
+    # one-hot rows of A: C row = one fp8 product per column, exact in bf16
+    A1 = np.zeros((M, K), dtype=np.uint8)
+    ks = rng.integers(0, K, M)
+    A1[np.arange(M), ks] = rng.choice(INT_CODES[1:], M)
+    sfA = np.ldexp(1.0, rng.integers(-3, 4, (M, K // 128))).astype(np.float32)
+    assert_bitwise(run_dense(A1, w.B, sfA, w.sfB), oracle.gemm_nt(A1, w.B, sfA, w.sfB), "one-hot")
+    # identity B
+    I = np.zeros((K, K), dtype=np.uint8)
+    I[np.arange(K), np.arange(K)] = 0x38
+    ones = np.ones((3, 3), dtype=np.float32)
+    assert_bitwise(run_dense(w.A, I, w.sfA, ones), oracle.gemm_nt(w.A, I, w.sfA, ones), "identity")
+    # doubling a scale row of A doubles that output row exactly
+    g0 = run_dense(w.A, w.B, w.sfA, w.sfB)
+    sf2 = w.sfA.copy()
+    sf2[7] *= 2
+    sf2[64] *= 0.5
+    g1 = run_dense(w.A, w.B, sf2, w.sfB)
+    f0, f1 = gu_bf16(g0), gu_bf16(g1)
+    assert np.array_equal(f1[7], 2 * f0[7]) and np.array_equal(f1[64], 0.5 * f0[64])
+    keep = [i for i in range(M) if i not in (7, 64)]
+    assert np.array_equal(g1[keep], g0[keep])
+
+
+def gu_bf16(b):
+    from tests.parity import bf16_to_f64
+    return bf16_to_f64(b)
+
+
+def test_dense_deterministic():
+    w = synth.workload("dec2112")
+    a = run_dense(w.A, w.B, w.sfA, w.sfB, seed=3)
+    b = run_dense(w.A, w.B, w.sfA, w.sfB, seed=4)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["dec2112", "dec32768"])
+def test_decode_workloads_full(name):
+    w = synth.workload(name)
+    g = run_dense(w.A, w.B, w.sfA, w.sfB)
+    rep = assert_parity(g, oracle.gemm_nt(w.A, w.B, w.sfA, w.sfB), what=name)
+    print(name, rep)
+
+
+def test_decode_workloads_integer_exact_bitwise():
+    for (M, N, K) in [(64, 2112, 7168), (64, 32768, 512)]:
+        rng = np.random.default_rng(N)
+        A, B, sfA, sfB = int_operands(rng, M, N, K)
+        g = run_dense(A, B, sfA, sfB)
+        assert_bitwise(g, oracle.gemm_nt(A, B, sfA, sfB), what=f"int {M}x{N}x{K}")
+
+
+def test_prefill_workload_sampled():
+    w = synth.workload("prefill")
+    M, N, K = w.shape
+    g = run_dense(w.A, w.B, w.sfA, w.sfB)
+    rng = np.random.default_rng(99)
+    mi, ni = sample_positions(rng, M, N)
+    r = oracle.gemm_nt_at(w.A, w.B, w.sfA, w.sfB, mi, ni)
+    rep = assert_parity(g[mi, ni], r, what="prefill sampled")
+    print("prefill sampled:", rep)
+
+
+def test_prefill_integer_exact_sampled_bitwise():
+    M, N, K = 4096, 7168, 18432
+    rng = np.random.default_rng(4096)
+    A = rng.choice(INT_CODES, size=(M, K)).astype(np.uint8)
+    B = rng.choice(INT_CODES, size=(N, K)).astype(np.uint8)
+    sfA = np.ones((M, K // 128), dtype=np.float32)
+    sfB = np.ones((N // 128, K // 128), dtype=np.float32)
+    g = run_dense(A, B, sfA, sfB)
+    mi, ni = sample_positions(rng, M, N, n_random=2000)
+    assert_bitwise(g[mi, ni], oracle.gemm_nt_at(A, B, sfA, sfB, mi, ni), "prefill int")
+
+
+# ------------------------------------------------------------------ contiguous
+
+
+def run_contiguous(A, B, sfA, sfB, m_indices, seed=2):
+    M_total, K = A.shape
+    G, N, _ = B.shape
+    out = gu.Guarded((M_total, N), seed)
+    gu.announce(f"contiguous M_total={M_total} N={N} K={K} G={G}")
+    dg().m_grouped_fp8_gemm_nt_contiguous(gu.codes(A), gu.codes(B), out.out, gu.dev(sfA),
+                                          gu.dev(sfB), gu.dev(m_indices.astype(np.int32)))
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside C"
+    return out.result(), out.initial()
+
+
+def check_contiguous_full(w, g, init, exact=False):
+    r, produced = oracle.grouped_contiguous(w.A, w.B, w.sfA, w.sfB, w.m_indices)
+    assert np.array_equal(g[~produced], init[~produced]), "pad rows touched"
+    if exact:
+        assert_bitwise(g[produced], r[produced], "contiguous int")
+        return None
+    return assert_parity(g[produced], r[produced], what="contiguous")
+
+
+def test_contiguous_small_with_empty_experts():
+    counts = np.array([5, 0, 128, 129, 0, 1, 300, 0], dtype=np.int32)
+    w = synth.contiguous(8, 256, 384, 0, seed_base=888000, counts=counts)
+    g, init = run_contiguous(w.A, w.B, w.sfA, w.sfB, w.m_indices)
+    print("contiguous small:", check_contiguous_full(w, g, init))
+
+
+def test_contiguous_unaligned_mixed_and_bad_ids_bitwise():
+    rng = np.random.default_rng(17)
+    G, N, K, M_total = 5, 144, 256, 300
+    # experts interleaved inside 128-row groups, ids out of range, no alignment
+    m_indices = rng.integers(-2, G + 2, size=M_total).astype(np.int32)
+    m_indices[:40] = 3
+    A, B, sfA, sfB = int_operands(rng, M_total, N, K, G=G)
+
+    class W: pass
+    w = W()
+    w.A, w.B, w.sfA, w.sfB, w.m_indices = A, B, sfA, sfB, m_indices
+    g, init = run_contiguous(A, B, sfA, sfB, m_indices)
+    check_contiguous_full(w, g, init, exact=True)
+
+
+def test_contiguous_nan_pad_rows_never_read():
+    counts = np.array([3, 130, 0, 64], dtype=np.int32)
+    w = synth.contiguous(4, 128, 256, 0, seed_base=889000, counts=counts,
+                         pad_code=synth.FP8_NAN_CODE)
+    assert np.any(w.A == synth.FP8_NAN_CODE)
+    g, init = run_contiguous(w.A, w.B, w.sfA, w.sfB, w.m_indices)
+    check_contiguous_full(w, g, init)
+
+
+def test_contiguous_workload_sampled():
+    w = synth.workload("moe_cont")
+    M_total, N, K, G = w.shape
+    g, init = run_contiguous(w.A, w.B, w.sfA, w.sfB, w.m_indices)
+    pad = w.m_indices < 0
+    assert np.array_equal(g[pad], init[pad]), "pad rows touched"
+    rng = np.random.default_rng(7)
+    real_rows = np.nonzero(~pad)[0]
+    ri, ni = sample_positions(rng, real_rows.size, N)
+    ri = real_rows[ri]
+    # add the first and last row of every segment
+    firsts = [np.nonzero(w.m_indices == e)[0] for e in range(G) if w.counts[e] > 0]
+    edge = np.concatenate([[s[0], s[-1]] for s in firsts])
+    ri = np.concatenate([ri, np.repeat(edge, 32)])
+    ni = np.concatenate([ni, rng.integers(0, N, edge.size * 32)])
+    r = oracle.grouped_contiguous_at(w.A, w.B, w.sfA, w.sfB, w.m_indices, ri, ni)
+    rep = assert_parity(g[ri, ni], r, what="moe_cont sampled")
+    print("moe_cont sampled:", rep)
+
+
+# ------------------------------------------------------------------ masked
+
+
+def run_masked(A, B, sfA, sfB, masked_m, expected_m=None, seed=3):
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    out = gu.Guarded((G, M_max, N), seed)
+    gu.announce(f"masked G={G} M_max={M_max} N={N} K={K}")
+    dg().m_grouped_fp8_gemm_nt_masked(gu.codes(A), gu.codes(B), out.out, gu.dev(sfA),
+                                      gu.dev(sfB), gu.dev(np.asarray(masked_m, np.int32)),
+                                      expected_m)
+    torch.cuda.synchronize()
+    assert out.guards_intact(), "write outside C"
+    return out.result(), out.initial()
+
+
+def test_masked_small_edges():
+    masked_m = np.array([0, 200, 1, 129, 64, 65, 999, -4], dtype=np.int32)  # last two clamp
+    w = synth.masked(8, 200, 256, 384, seed_base=990000, masked_m=masked_m,
+                     pad_code=synth.FP8_NAN_CODE)
+    g, init = run_masked(w.A, w.B, w.sfA, w.sfB, w.masked_m)
+    r, produced = oracle.grouped_masked(w.A, w.B, w.sfA, w.sfB, w.masked_m)
+    assert np.array_equal(g[~produced], init[~produced]), "masked rows touched"
+    print("masked small:", assert_parity(g[produced], r[produced], what="masked small"))
+
+
+def test_masked_integer_exact_bitwise():
+    rng = np.random.default_rng(31)
+    G, M_max, N, K = 4, 96, 2112, 512
+    A, B, sfA, sfB = int_operands(rng, G * M_max, N, K, G=G)
+    A = A.reshape(G, M_max, K)
+    sfA = sfA.reshape(G, M_max, K // 128)
+    masked_m = np.array([96, 33, 0, 64], dtype=np.int32)
+    for em in (None, 16, 96):
+        g, init = run_masked(A, B, sfA, sfB, masked_m, expected_m=em)
+        r, produced = oracle.grouped_masked(A, B, sfA, sfB, masked_m)
+        assert np.array_equal(g[~produced], init[~produced])
+        assert_bitwise(g[produced], r[produced], "masked int")
+
+
+def test_masked_workload_sampled():
+    w = synth.workload("moe_mask", pad_code=synth.FP8_NAN_CODE)
+    G, M_max, N, K = w.shape
+    g, init = run_masked(w.A, w.B, w.sfA, w.sfB, w.masked_m)
+    produced = np.arange(M_max)[None, :] < w.masked_m[:, None]
+    assert np.array_equal(g[~produced], init[~produced]), "masked rows touched"
+    rng = np.random.default_rng(8)
+    e_all, m_all = np.nonzero(produced)
+    pick = rng.integers(0, e_all.size, 6000)
+    ei, mi = e_all[pick], m_all[pick]
+    ni = rng.integers(0, N, pick.size)
+    # last valid row of every expert, and column block edges
+    last = [(e, w.masked_m[e] - 1) for e in range(G) if w.masked_m[e] > 0]
+    le = np.repeat([x[0] for x in last], 16)
+    lm = np.repeat([x[1] for x in last], 16)
+    ln = np.tile(np.array([0, 127, 128, 255, 256, 1023, 1024, N - 129, N - 128, N - 1,
+                           64, 63, 2047, 2048, 4095, 4096]), len(last))
+    ei, mi, ni = (np.concatenate([ei, le]), np.concatenate([mi, lm]), np.concatenate([ni, ln]))
+    r = oracle.grouped_masked_at(w.A, w.B, w.sfA, w.sfB, w.masked_m, ei, mi, ni)
+    rep = assert_parity(g[ei, mi, ni], r, what="moe_mask sampled")
+    print("moe_mask sampled:", rep)
