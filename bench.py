@@ -1,0 +1,343 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 block-scaled GEMM library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+A step is one pass of every GEMM in the workload over one batch of synthetic
+inputs already resident in HBM. The default workload is the pair of memory-bound
+decode shapes at M = 64 (64x2112x7168 and 64x32768x512, the shapes of the launch
+article's benchmark table, section 2.1); the metric is achieved algorithmic HBM
+throughput in GB/s. Other workloads (--workload prefill | moe_cont | moe_mask |
+small) report TFLOPS against the dense FP8 MFMA peak.
+
+Timing: W untimed warmup steps, then exactly K steps between two synchronisations.
+The K launches of each GEMM run back to back between a pair of HIP events
+(torch.cuda.Event, on the stream the kernels are launched on), which gives each
+kernel's average launch duration. Input and output buffers rotate over enough
+copies that their total exceeds 512 MB, so neither L2 nor the 256 MB MALL holds
+the previous step's operands.
+
+Prints one JSON line. The roofline object covers the kernel with the largest total
+time: algorithmic bytes (or FLOPs) per launch / its average event-timed duration
+against MI355X's published peak (HBM 8 TB/s; dense FP8 MFMA 5.0 PFLOP/s).
+cpu_baseline is the CPU oracle timed on the host's cores over the whole step
+(reported as a baseline only), and that same leg compares the GPU outputs of the
+last timed step with the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+ROTATE_BYTES = 512 * 1024 * 1024
+METRIC = "FP8 block-scaled GEMM TFLOPS (%MFMA peak) and GB/s at M=64 (%HBM), 1 MI355X"
+
+WORKLOADS = {
+    "decode": ["dec2112", "dec32768"],
+    "prefill": ["prefill"],
+    "moe_cont": ["moe_cont"],
+    "moe_mask": ["moe_mask"],
+    "small": ["small"],
+}
+DESCRIPTIONS = {
+    "decode": "dense NT decode, M=64: 64x2112x7168 + 64x32768x512",
+    "prefill": "dense NT prefill 4096x7168x18432",
+    "moe_cont": "MoE grouped contiguous, 32 experts, N=4096, K=7168, 8192 Zipf-routed tokens",
+    "moe_mask": "MoE grouped masked, 32 experts x 256 rows, N=7168, K=2048",
+    "small": "dense NT 128x256x512",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_block_scaled_dg_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class Gemm:
+    """One GEMM of the workload: host inputs, device copies, algorithmic work."""
+
+    def __init__(self, name, w):
+        import numpy as np
+        self.name, self.w = name, w
+        self.kind = type(w).__name__.lower()
+        if self.kind == "dense":
+            M, N, K = w.shape
+            Mv, Ga, G = M, 1, 1
+            meta = 0
+        elif self.kind == "contiguous":
+            M, N, K, G = w.shape
+            Mv = int(w.counts.sum())
+            Ga = int((w.counts > 0).sum())
+            meta = 4 * M
+        else:
+            G, M, N, K = w.shape
+            Mv = int(np.clip(w.masked_m, 0, M).sum())
+            Ga = int((np.clip(w.masked_m, 0, M) > 0).sum())
+            meta = 4 * G
+        KB, NB = K // 128, (N + 127) // 128
+        self.flops = 2.0 * Mv * N * K
+        self.bytes = (Mv * K + Ga * N * K + 4 * Mv * KB + 4 * Ga * NB * KB + 2 * Mv * N + meta)
+        self.shape = dict(M=M, N=N, K=K, G=G, valid_rows=Mv, active_experts=Ga)
+        self.footprint = (w.A.nbytes + w.B.nbytes + w.sfA.nbytes + w.sfB.nbytes
+                          + (M * N * 2 if self.kind != "masked" else G * M * N * 2))
+
+    def upload(self, copies: int):
+        import torch
+        dev = torch.device("cuda:0")
+
+        def t(x):
+            return torch.from_numpy(x).to(dev)
+
+        base = dict(A=t(self.w.A).view(torch.float8_e4m3fn), B=t(self.w.B).view(torch.float8_e4m3fn),
+                    sfA=t(self.w.sfA), sfB=t(self.w.sfB))
+        if self.kind == "contiguous":
+            base["idx"] = t(self.w.m_indices)
+            cshape = (self.w.A.shape[0], self.w.B.shape[1])
+        elif self.kind == "masked":
+            base["idx"] = t(self.w.masked_m)
+            cshape = (self.w.A.shape[0], self.w.A.shape[1], self.w.B.shape[1])
+        else:
+            cshape = (self.w.A.shape[0], self.w.B.shape[0])
+        self.sets = []
+        for i in range(copies):
+            s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
+            s["C"] = torch.zeros(cshape, dtype=torch.bfloat16, device=dev)
+            self.sets.append(s)
+
+    def launch(self, i: int):
+        import fp8_block_scaled_dg_amd as dg
+        s = self.sets[i % len(self.sets)]
+        if self.kind == "dense":
+            dg.fp8_gemm_nt(s["A"], s["B"], s["C"], s["sfA"], s["sfB"])
+        elif self.kind == "contiguous":
+            dg.m_grouped_fp8_gemm_nt_contiguous(s["A"], s["B"], s["C"], s["sfA"], s["sfB"],
+                                                s["idx"])
+        else:
+            dg.m_grouped_fp8_gemm_nt_masked(s["A"], s["B"], s["C"], s["sfA"], s["sfB"], s["idx"],
+                                            int(self.w.masked_m.mean()))
+
+
+def oracle_leg(gemms, last_set: int, budget_macs: float = 4e9):
+    """CPU baseline: the oracle over the step's produced outputs -- every output when a
+    GEMM is at most budget_macs multiply-adds, else a seeded sample of whole rows --
+    timed on the host cores and scaled to the whole step; and the comparison of the
+    last timed step's GPU outputs with it at the same positions."""
+    import numpy as np
+    import torch
+    import oracle
+    from tests.parity import report
+
+    per_step, checks, samples = 0.0, {}, []
+    for g in gemms:
+        w = g.w
+        N, K = g.shape["N"], g.shape["K"]
+        if g.kind == "dense":
+            rows = np.arange(g.shape["M"])
+        elif g.kind == "contiguous":
+            rows = np.nonzero(w.m_indices >= 0)[0]
+        else:
+            M_max = g.shape["M"]
+            prod = np.arange(M_max)[None, :] < np.clip(w.masked_m, 0, M_max)[:, None]
+            rows = np.nonzero(prod.ravel())[0]  # flat e * M_max + m
+        n_rows = rows.size
+        take = int(min(n_rows, max(1, budget_macs // (N * K))))
+        if take < n_rows:
+            rows = np.sort(np.random.default_rng(12345).choice(rows, take, replace=False))
+        ri = np.repeat(rows, N).astype(np.int64)
+        ni = np.tile(np.arange(N, dtype=np.int64), rows.size)
+        reps, dt = 0, 0.0
+        while reps == 0 or dt < 1.0:  # repeat short samples for a stable time
+            t0 = time.perf_counter()
+            if g.kind == "dense":
+                r = oracle.gemm_nt_at(w.A, w.B, w.sfA, w.sfB, ri, ni)
+            elif g.kind == "contiguous":
+                r = oracle.grouped_contiguous_at(w.A, w.B, w.sfA, w.sfB, w.m_indices, ri, ni)
+            else:
+                M_max = g.shape["M"]
+                r = oracle.grouped_masked_at(w.A, w.B, w.sfA, w.sfB, w.masked_m, ri // M_max,
+                                             ri % M_max, ni)
+            dt += time.perf_counter() - t0
+            reps += 1
+        dt /= reps
+        per_step += dt * n_rows / rows.size
+        samples.append(f"{g.name}: {rows.size} of {n_rows} rows x {N} cols, {dt:.3f} s "
+                       f"(mean of {reps})")
+        C = g.sets[last_set % len(g.sets)]["C"].view(torch.int16).cpu().numpy().view(np.uint16)
+        gpu = C.reshape(-1, N)[ri, ni]
+        rep = report(gpu, r)
+        checks[g.name] = {k: rep[k] for k in ("n", "max_excess_rel", "bitwise_match", "n_fail",
+                                               "nan")}
+    return per_step, "; ".join(samples), checks
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (to calibrate HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import synth
+    import fp8_block_scaled_dg_amd as dg  # noqa: F401  (fails loudly if libdg.so is missing)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    gemms = [Gemm(n, synth.workload(n)) for n in WORKLOADS[args.workload]]
+    step_footprint = sum(g.footprint for g in gemms)
+    copies = max(1, -(-ROTATE_BYTES // step_footprint))
+    for g in gemms:
+        g.upload(copies)
+    torch.cuda.synchronize()
+
+    for s in range(args.warmup):
+        for g in gemms:
+            g.launch(s)
+    torch.cuda.synchronize()
+
+    # Timed region: the K steps' launches, grouped by GEMM (all K launches of one GEMM
+    # back to back on rotating buffers, then the next GEMM), bracketed by events on
+    # the launch stream: a group's elapsed time / K is that kernel's average launch
+    # duration (kernel time plus the back-to-back dispatch gap), and the total over
+    # all groups / K is the time of one step of the whole path.
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in gemms]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for j, g in enumerate(gemms):
+        ev[j][0].record()
+        for s in range(K):
+            g.launch(args.warmup + s)
+        ev[j][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+
+    kern = []
+    for j, g in enumerate(gemms):
+        ms = ev[j][0].elapsed_time(ev[j][1]) / K
+        kern.append(dict(name=g.name, shape=g.shape, avg_us=ms * 1e3,
+                         tflops=g.flops / (ms * 1e-3) / 1e12,
+                         gbs=g.bytes / (ms * 1e-3) / 1e9,
+                         alg_bytes=g.bytes, alg_flops=g.flops))
+    step_bytes = sum(g.bytes for g in gemms)
+    step_flops = sum(g.flops for g in gemms)
+    memory_bound = args.workload in ("decode",)
+    if memory_bound:
+        value, unit = step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = step_flops / (ms_per_step * 1e-3) / 1e12, "TFLOPS"
+
+    dom = max(range(len(gemms)), key=lambda j: kern[j]["avg_us"])
+    kd = kern[dom]
+    if memory_bound:
+        roof = dict(bound="hbm", achieved=kd["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=kd["gbs"] / HBM_PEAK_GBS)
+    else:
+        t_mem = kd["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = kd["alg_flops"] / (FP8_PEAK_TFLOPS * 1e12)
+        if t_mfma >= t_mem:
+            roof = dict(bound="mfma", achieved=kd["tflops"], peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=kd["tflops"] / FP8_PEAK_TFLOPS)
+        else:
+            roof = dict(bound="hbm", achieved=kd["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=kd["gbs"] / HBM_PEAK_GBS)
+    roof["kernel"] = kd["name"]
+    roof["traffic"] = measured_traffic(kd["name"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        per_step, sample, checks = oracle_leg(gemms, args.warmup + K - 1)
+        import oracle
+        cores = oracle.num_threads()
+        cpu_value = (step_bytes / per_step / 1e9) if memory_bound else (step_flops / per_step / 1e12)
+        cpu = dict(value=cpu_value, unit=unit, cores=cores, kind="oracle",
+                   sample=sample + f"; scaled to the whole step: {per_step:.2f} s",
+                   parity=checks)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) quantized to "
+                   "e4m3fn, A per 1x128, B per 128x128, power-of-two scales",
+                   "accumulate": "fp32", "output": "bf16", "parallelism": "single GPU",
+                   "rotation_copies": copies},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kern,
+        "wall_s": wall,
+        "kernel_source": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def copy_calibration(nbytes: int = 256 * 1024 * 1024, reps: int = 5):
+    """A plain device-to-device copy of known size: under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE per dispatch calibrate the HBM-traffic counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def measured_traffic(kernel_name: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch", {}).get(kernel_name)
+
+
+if __name__ == "__main__":
+    main()

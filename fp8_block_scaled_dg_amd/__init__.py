@@ -50,6 +50,11 @@ lib.dg_last_error_detail.argtypes = []
 lib.dg_describe_config.restype = ctypes.c_int
 lib.dg_describe_config.argtypes = [_i32, _i64, _i64, _i64, _i32, _i64, ctypes.c_char_p, _i64]
 
+lib.dg_num_configs.restype = _i32
+lib.dg_num_configs.argtypes = []
+lib.dg_config_name.restype = ctypes.c_char_p
+lib.dg_config_name.argtypes = [_i32]
+
 KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED = 0, 1, 2
 BLOCK = 128
 
@@ -161,5 +166,9 @@ def describe_config(kind: int, M: int, N: int, K: int, G: int = 1, expected_m: i
     return buf.value.decode()
 
 
-__all__ = ["fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+def config_names() -> list[str]:
+    return [lib.dg_config_name(i).decode() for i in range(lib.dg_num_configs())]
+
+
+__all__ = ["config_names", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
            "describe_config", "DGError", "lib", "LIB_PATH"]

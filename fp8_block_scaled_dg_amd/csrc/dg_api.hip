@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <set>
 #include <string>
@@ -20,6 +21,7 @@
 
 #include "../../include/dg.h"
 #include "gemm_kernel.hpp"
+#include "skinny_kernel.hpp"
 
 namespace dg {
 namespace {
@@ -36,55 +38,13 @@ dg_status fail(dg_status s, const char* fmt, ...) {
 
 // ---------------------------------------------------------------- config table
 
-enum CfgId : int { kCfg128x128 = 0, kCfg64x64 = 1, kNumCfg };
-
-struct CfgInfo {
-  const char* name;
-  int bm, bn;
-};
-const CfgInfo kCfgInfo[kNumCfg] = {
-    {"tile128x128_w2x2", 128, 128},
-    {"tile64x64_w2x2", 64, 64},
-};
+constexpr int64_t kCUs = 256;  // MI355X compute units (8 XCDs x 32)
 
 using Cfg128 = TileCfg<128, 128, 2, 2>;
 using Cfg64 = TileCfg<64, 64, 2, 2>;
 
-// Shape key -> configuration. kind: dense / contiguous / masked; m is the rows per
-// problem that matter for tiling (dense M, contiguous average segment, masked
-// expected_m).
-CfgId select_config(int kind, int64_t m, int64_t n, int64_t k, int32_t g) {
-  (void)n;
-  (void)k;
-  (void)g;
-  (void)kind;
-  if (m <= 64) return kCfg64x64;
-  return kCfg128x128;
-}
-
-bool print_configs() {
-  static const bool on = [] {
-    const char* e = getenv("DG_PRINT_CONFIGS");
-    return e && *e && strcmp(e, "0") != 0;
-  }();
-  return on;
-}
-
-void maybe_print(int kind, int64_t M, int64_t N, int64_t K, int32_t G, CfgId id) {
-  if (!print_configs()) return;
-  static std::mutex mu;
-  static std::set<std::tuple<int, int64_t, int64_t, int64_t, int32_t>> seen;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!seen.insert(std::make_tuple(kind, M, N, K, G)).second) return;
-  static const char* kinds[] = {"dense", "contiguous", "masked"};
-  fprintf(stderr, "[dg] %s M=%lld N=%lld K=%lld G=%d -> %s\n", kinds[kind], (long long)M,
-          (long long)N, (long long)K, G, kCfgInfo[id].name);
-}
-
-// ---------------------------------------------------------------- launching
-
 template <class Cfg, int KIND>
-dg_status launch_cfg(const Problem& p0, int64_t blocks, hipStream_t stream) {
+dg_status launch_tile(const Problem& p0, int64_t blocks, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
@@ -106,16 +66,188 @@ dg_status launch_cfg(const Problem& p0, int64_t blocks, hipStream_t stream) {
   return DG_OK;
 }
 
-template <int KIND>
-dg_status launch(CfgId id, const Problem& p, int64_t blocks, hipStream_t stream) {
-  switch (id) {
-    case kCfg128x128:
-      return launch_cfg<Cfg128, KIND>(p, blocks, stream);
-    case kCfg64x64:
-      return launch_cfg<Cfg64, KIND>(p, blocks, stream);
-    default:
-      return fail(DG_ERR_UNSUPPORTED_SHAPE, "no configuration %d", (int)id);
+// ---------------------------------------------------------------- split-K workspace
+//
+// Skinny launches with K split across workgroups keep fp32 partials and per-tile
+// arrival counters in library-owned device buffers, one set per (device, stream):
+// calls on one stream run in order and reuse them; calls on different streams never
+// share them. Every counter is zero between calls (zeroed when allocated, reset by
+// the kernel after use), so the counter buffer stays valid when a later call uses
+// more of it. Buffers only grow (an outgrown one is released in stream order) and
+// live until the process ends.
+struct Workspace {
+  void* partials = nullptr;
+  size_t partial_bytes = 0;
+  uint32_t* counters = nullptr;
+  size_t counter_count = 0;
+};
+
+dg_status grow(void** buf, size_t* have, size_t need, size_t elem, hipStream_t stream, bool zero) {
+  if (*have >= need) return DG_OK;
+  void* fresh = nullptr;
+  hipError_t e = hipMalloc(&fresh, need * elem);
+  if (e != hipSuccess)
+    return fail(DG_ERR_LAUNCH, "workspace hipMalloc(%zu): %s", need * elem, hipGetErrorString(e));
+  if (zero) {
+    e = hipMemsetAsync(fresh, 0, need * elem, stream);
+    if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "workspace clear: %s", hipGetErrorString(e));
   }
+  if (*buf) (void)hipFreeAsync(*buf, stream);
+  *buf = fresh;
+  *have = need;
+  return DG_OK;
+}
+
+dg_status get_workspace(hipStream_t stream, size_t partial_bytes, size_t counters,
+                        float** partials, uint32_t** counter_ptr) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, Workspace> table;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DG_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  Workspace& w = table[std::make_pair(dev, stream)];
+  dg_status st = grow(&w.partials, &w.partial_bytes, partial_bytes, 1, stream, false);
+  if (st != DG_OK) return st;
+  st = grow((void**)&w.counters, &w.counter_count, counters, sizeof(uint32_t), stream, true);
+  if (st != DG_OK) return st;
+  *partials = (float*)w.partials;
+  *counter_ptr = w.counters;
+  return DG_OK;
+}
+
+template <class Cfg>
+dg_status launch_skinny(const Problem& p0, int64_t blocks, hipStream_t stream) {
+  (void)blocks;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [] {
+    attr_err = hipFuncSetAttribute((const void*)skinny_kernel<Cfg>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
+  });
+  if (attr_err != hipSuccess)
+    return fail(DG_ERR_LAUNCH, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
+  SkinnyArgs a{};
+  a.p = p0;
+  const int KB = (int)(p0.K / kKBlock);
+  const int64_t tiles = (p0.N + Cfg::BN - 1) / Cfg::BN;
+  // K splits: as many as keep the grid within one workgroup per CU (a grid slightly
+  // above the CU count would double up a few CUs and stretch the tail), at most SMAX
+  // and at most one per K-block; then evened out so that no split is empty.
+  int64_t S = kCUs / tiles;
+  if (S > Cfg::SMAX) S = Cfg::SMAX;
+  if (S > KB) S = KB;
+  if (S < 1) S = 1;
+  const int KS = (int)((KB + S - 1) / S);
+  S = (KB + KS - 1) / KS;
+  a.S = (int32_t)S;
+  a.KS = KS;
+  a.p.tiles_m = 1;
+  a.p.tiles_n = (int32_t)tiles;
+  const int64_t grid = tiles * S;
+  if (grid > 0x7FFFFFFF) return fail(DG_ERR_UNSUPPORTED_SHAPE, "grid of %lld", (long long)grid);
+  if (S > 1) {
+    const size_t part = (size_t)grid * 64 * Cfg::BN * sizeof(float);
+    dg_status st = get_workspace(stream, part, (size_t)tiles, &a.ws, &a.counters);
+    if (st != DG_OK) return st;
+  }
+  hipLaunchKernelGGL((skinny_kernel<Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS_BYTES,
+                     stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
+  return DG_OK;
+}
+
+typedef dg_status (*Launcher)(const Problem&, int64_t, hipStream_t);
+
+struct CfgEntry {
+  const char* name;
+  Launcher dense, contiguous, masked;  // NULL where the configuration does not apply
+  int max_m;                            // skinny: rows it covers; 0 = any
+  int max_kb;                           // K/128 it supports; 0 = any
+};
+
+const CfgEntry kTable[] = {
+    {"tile128x128_w2x2", launch_tile<Cfg128, kDense>, launch_tile<Cfg128, kContiguous>,
+     launch_tile<Cfg128, kMasked>, 0, 0},
+    {"tile64x64_w2x2", launch_tile<Cfg64, kDense>, launch_tile<Cfg64, kContiguous>,
+     launch_tile<Cfg64, kMasked>, 0, 0},
+    {"skinny_w4_tn1_d3", launch_skinny<SkinnyCfg<4, 1, 3>>, nullptr, nullptr, 64, 0},
+    {"skinny_w4_tn1_d2", launch_skinny<SkinnyCfg<4, 1, 2>>, nullptr, nullptr, 64, 0},
+    {"skinny_w4_tn1_d5", launch_skinny<SkinnyCfg<4, 1, 5>>, nullptr, nullptr, 64, 0},
+    {"skinny_w4_tn1_d8", launch_skinny<SkinnyCfg<4, 1, 8>>, nullptr, nullptr, 64, 0},
+    {"skinny_w2_tn1_d3", launch_skinny<SkinnyCfg<2, 1, 3>>, nullptr, nullptr, 64, 0},
+    {"skinny_w2_tn1_d5", launch_skinny<SkinnyCfg<2, 1, 5>>, nullptr, nullptr, 64, 0},
+    {"skinny_w2_tn1_d8", launch_skinny<SkinnyCfg<2, 1, 8>>, nullptr, nullptr, 64, 0},
+    {"skinny_w8_tn1_d4", launch_skinny<SkinnyCfg<8, 1, 4>>, nullptr, nullptr, 64, 0},
+};
+constexpr int kNumCfg = (int)(sizeof(kTable) / sizeof(kTable[0]));
+
+int find_cfg(const char* name) {
+  for (int i = 0; i < kNumCfg; ++i)
+    if (strcmp(kTable[i].name, name) == 0) return i;
+  return -1;
+}
+
+Launcher launcher_for(int id, int kind) {
+  const CfgEntry& c = kTable[id];
+  return kind == kDense ? c.dense : kind == kContiguous ? c.contiguous : c.masked;
+}
+
+bool cfg_applies(int id, int kind, int64_t M, int64_t K) {
+  const CfgEntry& c = kTable[id];
+  if (!launcher_for(id, kind)) return false;
+  if (c.max_m && M > c.max_m) return false;
+  if (c.max_kb && K / kKBlock > c.max_kb) return false;
+  return true;
+}
+
+// Shape key -> configuration. m: rows that matter for tiling (dense M, contiguous
+// rows per expert, masked expected_m); M: rows the kernel must cover.
+int select_config(int kind, int64_t m, int64_t M, int64_t n, int64_t k, int32_t g) {
+  (void)g;
+  const char* forced = getenv("DG_FORCE_CONFIG");
+  if (forced && *forced) {
+    const int id = find_cfg(forced);
+    if (id >= 0 && cfg_applies(id, kind, M, k)) return id;
+  }
+  if (kind == kDense && M <= 64) {
+    // the launcher's split choice for 64-column tiles decides the pipeline depth:
+    // long K runs per workgroup keep 8 blocks in flight, short ones 2
+    const int64_t kb = k / kKBlock, tiles = (n + 63) / 64;
+    int64_t s = kCUs / tiles;
+    s = s > 8 ? 8 : (s < 1 ? 1 : s);
+    if (s > kb) s = kb;
+    const int64_t run = (kb + s - 1) / s;
+    return find_cfg(run >= 6 ? "skinny_w4_tn1_d8" : "skinny_w4_tn1_d2");
+  }
+  if (m <= 64) return find_cfg("tile64x64_w2x2");
+  return find_cfg("tile128x128_w2x2");
+}
+
+bool print_configs() {
+  static const bool on = [] {
+    const char* e = getenv("DG_PRINT_CONFIGS");
+    return e && *e && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void maybe_print(int kind, int64_t M, int64_t N, int64_t K, int32_t G, int id) {
+  if (!print_configs()) return;
+  static std::mutex mu;
+  static std::set<std::tuple<int, int64_t, int64_t, int64_t, int32_t>> seen;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!seen.insert(std::make_tuple(kind, M, N, K, G)).second) return;
+  static const char* kinds[] = {"dense", "contiguous", "masked"};
+  fprintf(stderr, "[dg] %s M=%lld N=%lld K=%lld G=%d -> %s\n", kinds[kind], (long long)M,
+          (long long)N, (long long)K, G, kTable[id].name);
+}
+
+dg_status launch(int kind, int id, const Problem& p, int64_t blocks, hipStream_t stream) {
+  Launcher l = launcher_for(id, kind);
+  if (!l) return fail(DG_ERR_UNSUPPORTED_SHAPE, "configuration %s does not apply", kTable[id].name);
+  return l(p, blocks, stream);
 }
 
 // ---------------------------------------------------------------- validation
@@ -179,9 +311,9 @@ dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA
   p.N = N;
   p.K = K;
   p.G = 1;
-  const CfgId id = select_config(kDense, M, N, K, 1);
+  const int id = select_config(kDense, M, M, N, K, 1);
   maybe_print(kDense, M, N, K, 1, id);
-  return launch<kDense>(id, p, 1, (hipStream_t)stream);
+  return launch(kDense, id, p, 1, (hipStream_t)stream);
 }
 
 dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const void* B, void* C,
@@ -207,9 +339,9 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const void* B, void
   p.N = N;
   p.K = K;
   p.G = G;
-  const CfgId id = select_config(kContiguous, M_total / G, N, K, G);
+  const int id = select_config(kContiguous, M_total / G, M_total, N, K, G);
   maybe_print(kContiguous, M_total, N, K, G, id);
-  return launch<kContiguous>(id, p, 1, (hipStream_t)stream);
+  return launch(kContiguous, id, p, 1, (hipStream_t)stream);
 }
 
 dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
@@ -238,10 +370,14 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
   p.K = K;
   p.G = G;
   const int64_t em = expected_m > 0 && expected_m < M_max ? expected_m : M_max;
-  const CfgId id = select_config(kMasked, em, N, K, G);
+  const int id = select_config(kMasked, em, M_max, N, K, G);
   maybe_print(kMasked, M_max, N, K, G, id);
-  return launch<kMasked>(id, p, G, (hipStream_t)stream);
+  return launch(kMasked, id, p, G, (hipStream_t)stream);
 }
+
+int32_t dg_num_configs(void) { return kNumCfg; }
+
+const char* dg_config_name(int32_t i) { return i >= 0 && i < kNumCfg ? kTable[i].name : nullptr; }
 
 dg_status dg_describe_config(int32_t kind, int64_t M, int64_t N, int64_t K, int32_t G,
                              int64_t expected_m, char* buf, int64_t len) {
@@ -249,8 +385,8 @@ dg_status dg_describe_config(int32_t kind, int64_t M, int64_t N, int64_t K, int3
   int64_t m = M;
   if (kind == kContiguous) m = G > 0 ? M / G : M;
   if (kind == kMasked) m = expected_m > 0 && expected_m < M ? expected_m : M;
-  const CfgId id = select_config(kind, m, N, K, G);
-  snprintf(buf, (size_t)len, "%s", kCfgInfo[id].name);
+  const int id = select_config(kind, m, M, N, K, G);
+  snprintf(buf, (size_t)len, "%s", kTable[id].name);
   return DG_OK;
 }
 

@@ -38,7 +38,8 @@
  *    thread-local message for the last failing call on the calling thread.
  *  - Zero-sized work (M, N or G*M_max == 0) returns DG_OK and launches nothing.
  *  - Environment: DG_PRINT_CONFIGS=1 prints the tile configuration chosen for each
- *    new (kind, shape) to stderr.
+ *    new (kind, shape) to stderr; DG_FORCE_CONFIG=<name> overrides the choice
+ *    (tuning only, see dg_config_name).
  */
 #ifndef DG_H_
 #define DG_H_
@@ -121,6 +122,15 @@ const char* dg_last_error_detail(void);
  */
 dg_status dg_describe_config(int32_t kind, int64_t M, int64_t N, int64_t K, int32_t G,
                              int64_t expected_m, char* buf, int64_t len);
+
+/*
+ * The compiled-in tile configurations, for tuning and diagnostics: their number and
+ * the name of configuration i (NULL when i is out of range). Setting the environment
+ * variable DG_FORCE_CONFIG=<name> makes every later call that the configuration can
+ * serve use it (calls it cannot serve keep the table's choice).
+ */
+int32_t dg_num_configs(void);
+const char* dg_config_name(int32_t i);
 
 #ifdef __cplusplus
 }

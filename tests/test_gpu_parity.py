@@ -92,7 +92,8 @@ def test_dense_integer_exact_bitwise(M, N, K):
     assert_bitwise(g, oracle.gemm_nt(A, B, sfA, sfB), what=f"int {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(65, 2112, 1024), (300, 528, 640), (1, 32, 128), (17, 4096, 256)])
+@pytest.mark.parametrize("M,N,K", [(65, 2112, 1024), (300, 528, 640), (1, 32, 128), (17, 4096, 256),
+                                   (64, 2112, 1664), (33, 7168, 2048)])
 def test_dense_gaussian_shapes(M, N, K):
     w = synth.dense(M, N, K, seed_base=777000 + M)
     g = run_dense(w.A, w.B, w.sfA, w.sfB)
@@ -314,3 +315,55 @@ def test_masked_workload_sampled():
     r = oracle.grouped_masked_at(w.A, w.B, w.sfA, w.sfB, w.masked_m, ei, mi, ni)
     rep = assert_parity(g[ei, mi, ni], r, what="moe_mask sampled")
     print("moe_mask sampled:", rep)
+
+
+# ------------------------------------------------------------------ every configuration
+
+
+@pytest.fixture
+def force_config(monkeypatch):
+    def set_cfg(name):
+        monkeypatch.setenv("DG_FORCE_CONFIG", name)
+    yield set_cfg
+
+
+def all_configs():
+    import fp8_block_scaled_dg_amd as m
+    return m.config_names()
+
+
+@pytest.mark.parametrize("cfg", all_configs())
+def test_every_config_dense_integer_exact(cfg, force_config):
+    force_config(cfg)
+    shapes = [(64, 2112, 1024), (37, 272, 384), (1, 16, 128), (64, 2112, 1664), (50, 1040, 7168)]
+    if not cfg.startswith("skinny"):
+        shapes += [(300, 400, 512), (129, 144, 256)]
+    for (M, N, K) in shapes:
+        rng = np.random.default_rng(M + N + K)
+        A, B, sfA, sfB = int_operands(rng, M, N, K)
+        g = run_dense(A, B, sfA, sfB)
+        assert_bitwise(g, oracle.gemm_nt(A, B, sfA, sfB), what=f"{cfg} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("cfg", [c for c in all_configs() if not c.startswith("skinny")])
+def test_every_config_grouped_integer_exact(cfg, force_config):
+    force_config(cfg)
+    rng = np.random.default_rng(3)
+    G, N, K = 3, 272, 384
+    counts = np.array([70, 0, 200], dtype=np.int32)
+    m_indices = synth.contiguous_layout(counts)
+    A, B, sfA, sfB = int_operands(rng, m_indices.size, N, K, G=G)
+
+    class W: pass
+    w = W()
+    w.A, w.B, w.sfA, w.sfB, w.m_indices = A, B, sfA, sfB, m_indices
+    g, init = run_contiguous(A, B, sfA, sfB, m_indices)
+    check_contiguous_full(w, g, init, exact=True)
+    M_max = 150
+    Am, _, sfAm, _ = int_operands(rng, G * M_max, N, K, G=G)
+    Am, sfAm = Am.reshape(G, M_max, K), sfAm.reshape(G, M_max, K // 128)
+    masked_m = np.array([150, 0, 77], dtype=np.int32)
+    g, init = run_masked(Am, B, sfAm, sfB, masked_m)
+    r, produced = oracle.grouped_masked(Am, B, sfAm, sfB, masked_m)
+    assert np.array_equal(g[~produced], init[~produced])
+    assert_bitwise(g[produced], r[produced], f"{cfg} masked")
