@@ -10,12 +10,16 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libdg.so")
 SOURCES = [os.path.join(CSRC, "dg_api.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, "gemm_kernel.hpp"), os.path.join(ROOT, "include", "dg.h")]
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".hpp")] + [
+    os.path.join(ROOT, "include", "dg.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
     # no packed-fp32 VALU instructions (v_pk_*_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the per-K-block promotion reads every partial
+    # with VALU FMAs, which cannot take AGPR operands
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -21,6 +21,7 @@
 
 #include "../../include/dg.h"
 #include "gemm_kernel.hpp"
+#include "pipe_kernel.hpp"
 #include "skinny_kernel.hpp"
 
 namespace dg {
@@ -65,6 +66,23 @@ dg_status launch_tile(const Problem& p0, int64_t blocks, hipStream_t stream) {
   if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
   return DG_OK;
 }
+
+template <class Cfg, int KIND>
+dg_status launch_pipe(const Problem& p0, int64_t blocks, hipStream_t stream) {
+  Problem p = p0;
+  p.tiles_m = (int32_t)((p.M + Cfg::BM - 1) / Cfg::BM);
+  p.tiles_n = (int32_t)((p.N + Cfg::BN - 1) / Cfg::BN);
+  const int64_t grid = blocks * p.tiles_m * p.tiles_n;
+  if (grid <= 0) return DG_OK;
+  if (grid > 0x7FFFFFFF) return fail(DG_ERR_UNSUPPORTED_SHAPE, "grid of %lld tiles", (long long)grid);
+  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
+  return DG_OK;
+}
+
+using Pipe256x128 = PipeCfg<256, 128>;
+using Pipe128x256 = PipeCfg<128, 256>;
 
 // ---------------------------------------------------------------- split-K workspace
 //
@@ -167,11 +185,19 @@ struct CfgEntry {
   int max_kb;                           // K/128 it supports; 0 = any
 };
 
+// The pipelined kernel addresses a tile's rows with 32-bit offsets below 256 * K
+// bytes; this bound keeps them under 2^31.
+constexpr int kPipeMaxKB = (1 << 22) / kKBlock;
+
 const CfgEntry kTable[] = {
     {"tile128x128_w2x2", launch_tile<Cfg128, kDense>, launch_tile<Cfg128, kContiguous>,
      launch_tile<Cfg128, kMasked>, 0, 0},
     {"tile64x64_w2x2", launch_tile<Cfg64, kDense>, launch_tile<Cfg64, kContiguous>,
      launch_tile<Cfg64, kMasked>, 0, 0},
+    {"pipe256x128", launch_pipe<Pipe256x128, kDense>, launch_pipe<Pipe256x128, kContiguous>,
+     launch_pipe<Pipe256x128, kMasked>, 0, kPipeMaxKB},
+    {"pipe128x256", launch_pipe<Pipe128x256, kDense>, launch_pipe<Pipe128x256, kContiguous>,
+     launch_pipe<Pipe128x256, kMasked>, 0, kPipeMaxKB},
     {"skinny_w4_tn1_d3", launch_skinny<SkinnyCfg<4, 1, 3>>, nullptr, nullptr, 64, 0},
     {"skinny_w4_tn1_d2", launch_skinny<SkinnyCfg<4, 1, 2>>, nullptr, nullptr, 64, 0},
     {"skinny_w4_tn1_d5", launch_skinny<SkinnyCfg<4, 1, 5>>, nullptr, nullptr, 64, 0},
@@ -221,8 +247,8 @@ int select_config(int kind, int64_t m, int64_t M, int64_t n, int64_t k, int32_t 
     const int64_t run = (kb + s - 1) / s;
     return find_cfg(run >= 6 ? "skinny_w4_tn1_d8" : "skinny_w4_tn1_d2");
   }
-  if (m <= 64) return find_cfg("tile64x64_w2x2");
-  return find_cfg("tile128x128_w2x2");
+  if (k / kKBlock > kPipeMaxKB) return find_cfg("tile128x128_w2x2");
+  return find_cfg("pipe128x256");
 }
 
 bool print_configs() {

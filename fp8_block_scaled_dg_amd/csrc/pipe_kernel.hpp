@@ -1,0 +1,463 @@
+// pipe_kernel.hpp -- compute-bound FP8 block-scaled GEMM kernel for CDNA4 (gfx950).
+//
+// One workgroup of 8 waves (two per SIMD) computes one BM x BN output tile
+// (256x128 or 128x256); each wave owns a 64x64 sub-tile as 2x2 tiles of 32x32.
+//
+// Arithmetic (DeepGEMM launch article, deepseek.csdn.net, section 1.2 "precision
+// safeguards": FP8 products of one 128-wide K-block are promoted to FP32 and
+// scaled before the accumulation across K-blocks):
+//   level 1: two chained v_mfma_f32_32x32x64_f8f6f4 (K 0..63 and 64..127 of the
+//            block) give the block's unscaled fp32 partial P of a 32x32 tile;
+//   level 2: acc += P * (sfA[m][kb] * sfB[n/128][kb]) in fp32 VGPRs.
+// The MFMA is issued with B as its first operand and A as its second, so every
+// lane of a 32x32 result holds one row m (lane % 32) and 16 columns n. All 16
+// values of a lane then share one scale product per K-block, and the 32 columns
+// of a tile always sit in one 128-column sfB block.
+//
+// Operand movement: global memory -> LDS by direct-to-LDS DMA (global_load_lds,
+// 16 bytes per lane), no register staging. Three LDS stages hold K-blocks kb,
+// kb+1, kb+2; while block kb is multiplied, kb+1 and kb+2 are in flight. Each
+// stage is its own __shared__ array so that the compiler can tell a DMA into one
+// stage from a read of another; the K loop is unrolled by three so every stage
+// index is a compile-time constant. Once per K-block each wave waits until its own
+// DMAs of the next block have landed (vmcnt), then one workgroup barrier makes
+// every wave's DMAs visible and retires all reads of the stage that the following
+// DMA overwrites. The barrier sits in the middle of a block's MFMAs, and the next
+// block's first fragments are read behind it, so LDS reads spread over the block
+// instead of bursting after the barrier.
+//
+// LDS rows are 128 bytes; the 16-byte chunk c of row r sits at c ^ swz(r), so
+// the 16 lanes served together by a 128-bit LDS read hit disjoint banks. The DMA
+// applies the swizzle on the global side: lane l of an instruction fills LDS row
+// 8q + l/8, chunk l%8, from global chunk (l%8) ^ swz(row).
+//
+// Out-of-range rows (M or N tails) are clamped to the last row for loading; the
+// epilogue stores only produced rows and in-range columns.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace dg {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <int BM_, int BN_>
+struct PipeCfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WAVES_M = BM / 64, WAVES_N = BN / 64;
+  static constexpr int NW = WAVES_M * WAVES_N;
+  static constexpr int NT = NW * 64;
+  static constexpr int TM = 2, TN = 2;                 // 32x32 tiles per wave (fixed)
+  static constexpr int A_DMA = BM * kKBlock / 1024 / NW;  // 1 KB DMA instructions per wave
+  static constexpr int B_DMA = BN * kKBlock / 1024 / NW;
+  static constexpr int RPW = BM / NW;                  // sfA rows loaded by one wave
+  static constexpr int NBT = BN / 128;                 // sfB blocks per tile
+  static constexpr int DMA_PER_KB = A_DMA + B_DMA + 2;  // + sfA + sfB
+  static constexpr int OFF_B = BM * kKBlock;
+  static constexpr int OFF_SA = (BM + BN) * kKBlock;   // 256 bytes per wave
+  static constexpr int OFF_SB = OFF_SA + NW * 256;     // 256 bytes per wave
+  static constexpr int STAGE = OFF_SB + NW * 256;
+  // M-tiles per raster group: 32 consecutive tiles cover 1024 A rows x 1024 B rows
+  static constexpr int GROUP_M = 1024 / BM;
+  static_assert(NW == 8, "two waves per SIMD");
+  static_assert(BN % 128 == 0, "tile columns nest in 128-column scale blocks");
+  static_assert(A_DMA >= 1 && B_DMA >= 1 && RPW <= 64 && 64 % RPW == 0, "DMA split");
+};
+
+constexpr int kPipeStageBytes = 53248;  // (256 + 128) * 128 + 2 * 8 * 256
+static_assert(PipeCfg<256, 128>::STAGE == kPipeStageBytes, "stage size");
+static_assert(PipeCfg<128, 256>::STAGE == kPipeStageBytes, "stage size");
+
+__shared__ __align__(16) uint8_t pipe_stage0[kPipeStageBytes];
+__shared__ __align__(16) uint8_t pipe_stage1[kPipeStageBytes];
+__shared__ __align__(16) uint8_t pipe_stage2[kPipeStageBytes];
+
+template <int S>
+__device__ __forceinline__ uint8_t* pipe_stage() {
+  return S == 0 ? pipe_stage0 : (S == 1 ? pipe_stage1 : pipe_stage2);
+}
+
+#define DG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with vmcnt = n and lgkmcnt = 0 (expcnt left at its maximum).
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+}
+
+// blockIdx -> position in the tile order. Workgroups are dealt to the 8 XCDs
+// round robin; this gives XCD x a contiguous range of the order so that the
+// tiles it runs at the same time share A rows and B columns in its L2.
+__device__ __forceinline__ int xcd_tile_order(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7, x = b & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
+// Grouped raster: GROUP_M consecutive M-tiles sweep all N-tiles together.
+template <int GM>
+__device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = GM * tiles_n;
+  const int group = t / per_group;
+  const int first = group * GM;
+  const int gsize = tiles_m - first < GM ? tiles_m - first : GM;
+  const int idx = t - group * per_group;
+  tm = first + idx % gsize;
+  tn = idx / gsize;
+}
+
+// DMA sources of one thread: buffer resources for the tile's rows (wave-uniform,
+// SGPRs) plus 32-bit per-lane byte offsets; the K-block offset goes in the
+// instruction's scalar offset.
+template <class Cfg>
+struct PipeThread {
+  __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, sa_rsrc, sb_rsrc;
+  uint32_t a_off[Cfg::A_DMA];
+  uint32_t b_off[Cfg::B_DMA];
+  uint32_t sa_off, sb_off;
+};
+
+// Raw buffer over [p, p + 2^31): the offsets used stay below that.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+template <class Cfg, int S>
+__device__ __forceinline__ void pipe_issue(const PipeThread<Cfg>& th, int kb, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
+  uint8_t* st = pipe_stage<S>();
+  const int koff = kb * kKBlock;
+#pragma unroll
+  for (int q = 0; q < Cfg::A_DMA; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.a_rsrc, DG_LDS(st + (wave * Cfg::A_DMA + q) * 1024),
+                                             16, th.a_off[q], koff, 0, 0);
+#pragma unroll
+  for (int q = 0; q < Cfg::B_DMA; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        th.b_rsrc, DG_LDS(st + Cfg::OFF_B + (wave * Cfg::B_DMA + q) * 1024), 16, th.b_off[q], koff,
+        0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sa_rsrc, DG_LDS(st + Cfg::OFF_SA + wave * 256), 4,
+                                           th.sa_off, kb * 4, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sb_rsrc, DG_LDS(st + Cfg::OFF_SB + wave * 256), 4,
+                                           th.sb_off, kb * 4, 0, 0);
+#endif
+}
+
+// Byte address of stage S for the fragment reads. Stages 0 and 1 start below 64 KB,
+// so their base folds into the 16-bit offset of ds_read; stage 2 starts above it
+// and is added at run time from an opaque SGPR, so that the compiler does not keep
+// a second hoisted set of per-lane addresses for it.
+template <int S>
+__device__ __forceinline__ const uint8_t* read_base() {
+  if (S < 2) return pipe_stage<S>();
+  uint32_t off = 0;
+  asm volatile("" : "+s"(off));
+  return pipe_stage<S>() + off;
+}
+
+__device__ __forceinline__ v8i frag_at(const uint8_t* p, uint32_t lo, uint32_t hi) {
+  const v4u x = *(const v4u*)(p + lo);
+  const v4u y = *(const v4u*)(p + hi);
+  return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+}
+
+#define DG_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+__device__ __forceinline__ v16f mfma32(const v8i& b, const v8i& a, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
+}
+
+// acc[e] += p[e] * s for e in [E0, E0 + 8)
+template <int E0>
+__device__ __forceinline__ void promote8(v16f& acc, const v16f& p, float s) {
+#pragma unroll
+  for (int e = E0; e < E0 + 8; ++e) acc[e] = __builtin_fmaf(p[e], s, acc[e]);
+}
+
+// Per-lane LDS geometry of a wave's 64x64 sub-tile. A lane reads row (lane % 32)
+// of each 32-row tile; chunk pairs {2g, 2g+1} (K half 0) and {4+2g, 5+2g} (K half
+// 1), g = lane / 32. The swizzle depends on the row only through lane % 32 (tile
+// and wave offsets are multiples of 32 rows), so four byte offsets per operand
+// serve every tile; tile 1 is 4096 bytes further.
+template <class Cfg>
+struct PipeLane {
+  uint32_t va[4], vb[4];
+  int sa0_idx, sa1_idx, sb_idx;
+  __device__ __forceinline__ PipeLane(int wave, int lane) {
+    const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+    const int r32 = lane & 31, g = lane >> 5;
+    const int sw = swz(r32);
+    const int chunk[4] = {2 * g, 2 * g + 1, 4 + 2 * g, 5 + 2 * g};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t c = (uint32_t)((chunk[k] ^ sw) << 4);
+      va[k] = (uint32_t)(wm * 64 + r32) * kKBlock + c;
+      vb[k] = (uint32_t)Cfg::OFF_B + (uint32_t)(wn * 64 + r32) * kKBlock + c;
+    }
+    const int ra0 = wm * 64 + r32, ra1 = ra0 + 32;
+    sa0_idx = (ra0 / Cfg::RPW) * 64 + ra0 % Cfg::RPW;
+    sa1_idx = (ra1 / Cfg::RPW) * 64 + ra1 % Cfg::RPW;
+    sb_idx = wave * 64 + (wn * 64) / 128;
+  }
+};
+
+// Both K-half fragments of 32-row tile `tile` (0/1) of the operand whose per-lane
+// offsets are v.
+__device__ __forceinline__ void read_tile(const uint8_t* st, const uint32_t (&v)[4], int tile,
+                                          v8i& h0, v8i& h1) {
+  const uint8_t* p = st + tile * 32 * kKBlock;
+  h0 = frag_at(p, v[0], v[1]);
+  h1 = frag_at(p, v[2], v[3]);
+}
+
+// Fragments of A tile 0 and B tile 0 of a K-block: read one step ahead.
+struct Frag0 {
+  v8i a0, a1, b0, b1;
+};
+
+// One pipeline step for K-block kb held in stage S. On entry f holds the A-tile-0
+// and B-tile-0 fragments of kb (read during the previous step). Tiles are
+// multiplied in the order (0,0), (0,1), (1,0), (1,1), each as two chained MFMAs
+// (K halves); each tile's promotion runs in the shadow of the next tile's MFMAs and
+// the last tile's partial (carry) is promoted during the next step's first tile.
+// Halfway, once A tile 0 of kb is dead, the wave waits for its own DMAs of block
+// kb+1 and meets the others at the barrier: block kb+1 is then in LDS and every
+// read of block kb is done, so the DMA of block kb+3 refills kb's stage and the
+// fragments of kb+1 are read into the registers kb no longer needs.
+// Scheduling fences keep this order; the compiler inserts only the LDS waits.
+template <class Cfg, int S>
+__device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeLane<Cfg>& pl,
+                                          v16f (&acc)[2][2], Frag0& f, v16f& carry,
+                                          float& carry_s, int kb, int KB, int wave) {
+  const uint8_t* st = read_base<S>();
+  const uint8_t* nst = read_base<(S + 1) % 3>();
+  const v16f zero = {};
+
+  v8i b10, b11;
+  read_tile(st, pl.vb, 1, b10, b11);
+  const float sb = ((const float*)(pipe_stage<S>() + Cfg::OFF_SB))[pl.sb_idx];
+  const float sa0 = ((const float*)(pipe_stage<S>() + Cfg::OFF_SA))[pl.sa0_idx];
+  const float sa1 = ((const float*)(pipe_stage<S>() + Cfg::OFF_SA))[pl.sa1_idx];
+  DG_FENCE();
+  // tile (0,0) | carry
+  v16f p = mfma32(f.b0, f.a0, zero);
+  promote8<0>(acc[1][1], carry, carry_s);
+  DG_FENCE();
+  p = mfma32(f.b1, f.a1, p);
+  promote8<8>(acc[1][1], carry, carry_s);
+  DG_FENCE();
+  v8i a10, a11;
+  read_tile(st, pl.va, 1, a10, a11);
+  const float s0 = sa0 * sb, s1 = sa1 * sb;
+  DG_FENCE();
+  // tile (0,1) | (0,0)
+  v16f q = mfma32(b10, f.a0, zero);
+  promote8<0>(acc[0][0], p, s0);
+  DG_FENCE();
+  q = mfma32(b11, f.a1, q);
+  promote8<8>(acc[0][0], p, s0);
+  DG_FENCE();
+  // block kb+1 in LDS, block kb's stage free
+  wait_vm_lgkm0<Cfg::DMA_PER_KB>();
+  __builtin_amdgcn_s_barrier();
+  DG_FENCE();
+  pipe_issue<Cfg, S>(th, kb + 3 < KB ? kb + 3 : KB - 1, wave);
+  DG_FENCE();
+  read_tile(nst, pl.va, 0, f.a0, f.a1);
+  DG_FENCE();
+  // tile (1,0) | (0,1)
+  v16f r = mfma32(f.b0, a10, zero);
+  promote8<0>(acc[0][1], q, s0);
+  DG_FENCE();
+  r = mfma32(f.b1, a11, r);
+  promote8<8>(acc[0][1], q, s0);
+  DG_FENCE();
+  read_tile(nst, pl.vb, 0, f.b0, f.b1);
+  DG_FENCE();
+  // tile (1,1) | (1,0)
+  v16f t = mfma32(b10, a10, zero);
+  promote8<0>(acc[1][0], r, s1);
+  DG_FENCE();
+  t = mfma32(b11, a11, t);
+  promote8<8>(acc[1][0], r, s1);
+  DG_FENCE();
+  carry = t;
+  carry_s = s1;
+}
+
+// Multiplies one tile: rows [m0, m0+BM) of the view, columns [n0, n0+BN).
+// valid_rows bounds the rows that are stored; for the contiguous layout only rows
+// whose m_indices entry equals `expert` are stored.
+template <class Cfg, int KIND>
+__device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, int expert,
+                                          int valid_rows) {
+  constexpr int TM = Cfg::TM, TN = Cfg::TN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR addresses
+  const int64_t K = p.K, N = p.N;
+  const int KB = (int)(K / kKBlock);
+  const int NB = (int)((N + kKBlock - 1) / kKBlock);
+  const int nb0 = (int)(v.n0 / kKBlock);
+
+  // Offsets relative to the tile's first row stay below BM * K bytes (or BN * K);
+  // the host checks that this stays below 2^31.
+  PipeThread<Cfg> th;
+  {
+    th.a_rsrc = raw_rsrc(v.A + v.m0 * K);
+    th.b_rsrc = raw_rsrc(v.B + v.n0 * K);
+    th.sa_rsrc = raw_rsrc(v.sfA + v.m0 * KB);
+    th.sb_rsrc = raw_rsrc(v.sfB + (int64_t)nb0 * KB);
+    const int rsub = lane >> 3, c = lane & 7;
+    const int a_rows = (int)(v.rows - v.m0 < Cfg::BM ? v.rows - v.m0 : Cfg::BM);
+    const int b_rows = (int)(N - v.n0 < Cfg::BN ? N - v.n0 : Cfg::BN);
+#pragma unroll
+    for (int q = 0; q < Cfg::A_DMA; ++q) {
+      const int R = (wave * Cfg::A_DMA + q) * 8 + rsub;
+      const int row = R < a_rows ? R : a_rows - 1;
+      th.a_off[q] = (uint32_t)row * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+    }
+#pragma unroll
+    for (int q = 0; q < Cfg::B_DMA; ++q) {
+      const int R = (wave * Cfg::B_DMA + q) * 8 + rsub;
+      const int row = R < b_rows ? R : b_rows - 1;
+      th.b_off[q] = (uint32_t)row * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+    }
+    int arow = wave * Cfg::RPW + (lane % Cfg::RPW);
+    if (arow >= a_rows) arow = a_rows - 1;
+    th.sa_off = (uint32_t)arow * (uint32_t)KB * 4u;
+    int nb = lane < Cfg::NBT ? lane : Cfg::NBT - 1;
+    if (nb0 + nb >= NB) nb = NB - 1 - nb0;
+    th.sb_off = (uint32_t)nb * (uint32_t)KB * 4u;
+  }
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
+  v16f carry = {};
+  float carry_s = 0.f;
+  const PipeLane<Cfg> pl(wave, lane);
+  Frag0 f;
+
+  // prologue: blocks 0 and 1 in flight; once block 0 has landed everywhere, block
+  // 2 starts and the first fragments of block 0 are read
+  pipe_issue<Cfg, 0>(th, 0, wave);
+  pipe_issue<Cfg, 1>(th, KB > 1 ? 1 : KB - 1, wave);
+  DG_FENCE();
+  wait_vm_lgkm0<Cfg::DMA_PER_KB>();
+  __builtin_amdgcn_s_barrier();
+  DG_FENCE();
+  pipe_issue<Cfg, 2>(th, KB > 2 ? 2 : KB - 1, wave);
+  DG_FENCE();
+  read_tile(read_base<0>(), pl.va, 0, f.a0, f.a1);
+  read_tile(read_base<0>(), pl.vb, 0, f.b0, f.b1);
+  DG_FENCE();
+  int kb = 0;
+  for (; kb + 3 <= KB; kb += 3) {
+    pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, kb, KB, wave);
+    pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, kb + 1, KB, wave);
+    pipe_step<Cfg, 2>(th, pl, acc, f, carry, carry_s, kb + 2, KB, wave);
+  }
+  if (kb < KB) pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, kb, KB, wave);
+  if (kb + 1 < KB) pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, kb + 1, KB, wave);
+  promote8<0>(acc[1][1], carry, carry_s);
+  promote8<8>(acc[1][1], carry, carry_s);
+  // every DMA has landed before the LDS can be reused or released
+  DG_FENCE();
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  DG_FENCE();
+
+  // ---- epilogue: bf16 RNE; lane holds row (lane % 32) of each 32x32 tile and
+  // columns 8*(e/4) + 4*(lane/32) + e%4
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const int r32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = v.m0 + wm * 64 + i * 32 + r32;
+    bool ok = row < (int64_t)valid_rows;
+    if (KIND == kContiguous && ok) ok = p.m_indices[row] == expert;
+    if (!ok) continue;
+    uint16_t* crow = v.C + row * N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int64_t col = v.n0 + wn * 64 + j * 32 + 8 * e4 + 4 * g;
+        if (col < N) {
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 0]) |
+                              ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 2]) |
+                              ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 3]) << 16);
+          *(uint2*)(crow + col) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+}
+
+template <class Cfg, int KIND>
+__global__ void __launch_bounds__(Cfg::NT) pipe_kernel(Problem p) {
+  const int t = xcd_tile_order(blockIdx.x, gridDim.x);
+  const int NB = (int)((p.N + kKBlock - 1) / kKBlock);
+  const int KB = (int)(p.K / kKBlock);
+  TileView v;
+  int tm, tn;
+  if (KIND == kMasked) {
+    const int per_expert = p.tiles_m * p.tiles_n;
+    const int e = t / per_expert;
+    grouped_tile<Cfg::GROUP_M>(t - e * per_expert, p.tiles_m, p.tiles_n, tm, tn);
+    int valid = p.masked_m[e];
+    valid = valid < 0 ? 0 : (valid > (int)p.M ? (int)p.M : valid);
+    v.m0 = (int64_t)tm * Cfg::BM;
+    v.n0 = (int64_t)tn * Cfg::BN;
+    if (v.m0 >= valid) return;  // whole tile past the expert's valid rows
+    v.A = p.A + (int64_t)e * p.M * p.K;
+    v.sfA = p.sfA + (int64_t)e * p.M * KB;
+    v.C = p.C + (int64_t)e * p.M * p.N;
+    v.B = p.B + (int64_t)e * p.N * p.K;
+    v.sfB = p.sfB + (int64_t)e * NB * KB;
+    v.rows = p.M;
+    pipe_tile<Cfg, KIND>(p, v, e, valid);
+    return;
+  }
+  grouped_tile<Cfg::GROUP_M>(t, p.tiles_m, p.tiles_n, tm, tn);
+  v.m0 = (int64_t)tm * Cfg::BM;
+  v.n0 = (int64_t)tn * Cfg::BN;
+  v.A = p.A;
+  v.sfA = p.sfA;
+  v.C = p.C;
+  v.rows = p.M;
+  if (KIND == kDense) {
+    v.B = p.B;
+    v.sfB = p.sfB;
+    pipe_tile<Cfg, KIND>(p, v, 0, (int)p.M);
+    return;
+  }
+  // contiguous: one pass per distinct expert id among the tile's rows, in
+  // increasing id order (one pass when segments are BM-aligned)
+  __shared__ int s_next;
+  int prev = -1;
+  for (;;) {
+    if (threadIdx.x == 0) s_next = 0x7FFFFFFF;
+    __syncthreads();
+    if (threadIdx.x < Cfg::BM) {
+      const int64_t row = v.m0 + threadIdx.x;
+      if (row < p.M) {
+        const int id = p.m_indices[row];
+        if (id > prev && id < p.G) atomicMin(&s_next, id);
+      }
+    }
+    __syncthreads();
+    const int e = s_next;
+    __syncthreads();
+    if (e == 0x7FFFFFFF) break;
+    v.B = p.B + (int64_t)e * p.N * p.K;
+    v.sfB = p.sfB + (int64_t)e * NB * KB;
+    pipe_tile<Cfg, KIND>(p, v, e, (int)p.M);
+    prev = e;
+  }
+}
+
+}  // namespace dg
