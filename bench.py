@@ -192,7 +192,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (to calibrate HBM counters)")
+    ap.add_argument("--gemm", default=None,
+                    help="run only this GEMM of the workload (for per-kernel counter runs)")
+    ap.add_argument("--summarize", metavar="MANIFEST", default=None,
+                    help="write profiles/ summaries from rocprofv3 outputs listed in MANIFEST "
+                         "(JSON); runs on the host, no GPU needed")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -210,7 +218,12 @@ def main():
     import fp8_block_scaled_dg_amd as dg  # noqa: F401  (fails loudly if libdg.so is missing)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    gemms = [Gemm(n, synth.workload(n)) for n in WORKLOADS[args.workload]]
+    names = WORKLOADS[args.workload]
+    if args.gemm is not None:
+        if args.gemm not in names:
+            sys.exit(f"--gemm {args.gemm} is not part of workload {args.workload}: {names}")
+        names = [args.gemm]
+    gemms = [Gemm(n, synth.workload(n)) for n in names]
     step_footprint = sum(g.footprint for g in gemms)
     copies = max(1, -(-ROTATE_BYTES // step_footprint))
     for g in gemms:
@@ -337,6 +350,128 @@ def measured_traffic(kernel_name: str):
     if rec.get("kernel_source") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch", {}).get(kernel_name)
+
+
+# ---------------------------------------------------------------- profile summaries
+#
+# A manifest (JSON) lists rocprofv3 output folders and the exact commands that made
+# them:
+#   {"trace": [{"label": "decode", "dir": ..., "bench_json": ..., "command": ...}],
+#    "traffic": {"calibration": {"fetch": DIR, "write": DIR, "command_fetch": ...,
+#                                "command_write": ...},
+#                "gemms": [{"gemm": "dec2112", "workload": "decode", "fetch": DIR,
+#                           "write": DIR, "command_fetch": ..., "command_write": ...}]}}
+# and --summarize turns them into short text summaries under profiles/.
+
+def _csv_rows(folder: str, suffix: str):
+    import csv
+    import glob
+    if not os.path.isabs(folder):
+        folder = os.path.join(ROOT, folder)
+    paths = sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True))
+    if not paths:
+        raise FileNotFoundError(f"no *{suffix} under {folder}")
+    with open(paths[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _ours(name: str) -> bool:
+    return "dg::" in name
+
+
+def _short(name: str) -> str:
+    return name.replace("void ", "").split("(")[0]
+
+
+def _per_dispatch(folder: str, counter: str):
+    """counter value per dispatch of each of our kernels, averaged over dispatches."""
+    acc, disp = {}, {}
+    for r in _csv_rows(folder, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        k = r["Kernel_Name"]
+        acc[k] = acc.get(k, 0.0) + float(r["Counter_Value"])
+        disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    return {k: acc[k] / len(disp[k]) for k in acc}, {k: len(v) for k, v in disp.items()}
+
+
+def summarize(manifest_path: str) -> None:
+    with open(manifest_path) as f:
+        man = json.load(f)
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    for t in man.get("trace", []):
+        stats = [r for r in _csv_rows(t["dir"], "kernel_stats.csv") if _ours(r["Name"])]
+        bj = t["bench_json"] if os.path.isabs(t["bench_json"]) else os.path.join(ROOT, t["bench_json"])
+        with open(bj) as f:
+            line = json.loads([x for x in f.read().splitlines() if x.startswith("{")][-1])
+        lines = [f"# Kernel trace: {line['config']['workload']}", "",
+                 "Command (repository root on the GPU host):", "",
+                 "    " + t["command"], "",
+                 "rocprofv3 --stats, our kernels (all dispatches, warm-up included):", "",
+                 "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for r in stats:
+            lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} |")
+        lines += ["", "bench.py line of the same run (HIP events around each GEMM's "
+                      "back-to-back launches):", ""]
+        for k in line["kernels"]:
+            lines.append(f"- {k['name']} {k['shape']}: {k['avg_us']:.2f} us per launch")
+        lines += [f"- value: {line['value']:.1f} {line['unit']}, "
+                  f"roofline frac {line['roofline']['frac']:.3f}", ""]
+        with open(os.path.join(out_dir, f"trace_{t['label']}.md"), "w") as f:
+            f.write("\n".join(lines))
+    tr = man.get("traffic")
+    if tr:
+        cal = tr["calibration"]
+        cf, _ = _per_dispatch(cal["fetch"], "FETCH_SIZE")
+        cw, _ = _per_dispatch(cal["write"], "WRITE_SIZE")
+        # the largest copy kernel in the calibration run is the 256 MiB copy
+        copy_kib = 256 * 1024
+        k_f = max(((v, k) for k, v in cf.items() if "copy" in k.lower() or "elementwise" in k),
+                  default=None)
+        if k_f is None:
+            k_f = max((v, k) for k, v in cf.items())
+        kern = k_f[1]
+        f_scale = copy_kib / cf[kern]
+        w_scale = copy_kib / cw[kern]
+        rec = {"kernel_source": kernel_source_hash(),
+               "calibration": {"kernel": _short(kern), "copy_bytes": copy_kib * 1024,
+                               "fetch_kib": cf[kern], "write_kib": cw[kern],
+                               "fetch_scale": f_scale, "write_scale": w_scale,
+                               "command_fetch": cal["command_fetch"],
+                               "command_write": cal["command_write"]},
+               "bytes_per_launch": {}, "detail": {}}
+        md = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+              "Calibration: a plain 256 MiB device copy reads "
+              f"{cf[kern]:.0f} KiB and writes {cw[kern]:.0f} KiB per dispatch "
+              f"(kernel `{_short(kern)}`); scale factors fetch {f_scale:.4f}, "
+              f"write {w_scale:.4f}.", "",
+              "    " + cal["command_fetch"], "    " + cal["command_write"], "",
+              "| GEMM | kernel | dispatches | fetch KiB | write KiB | scaled bytes |",
+              "|---|---|---|---|---|---|"]
+        for g in tr["gemms"]:
+            fv, fn = _per_dispatch(g["fetch"], "FETCH_SIZE")
+            wv, _ = _per_dispatch(g["write"], "WRITE_SIZE")
+            ours = [k for k in fv if _ours(k)]
+            if len(ours) != 1:
+                raise RuntimeError(f"{g['gemm']}: expected one of our kernels, got {ours}")
+            k = ours[0]
+            b = fv[k] * f_scale * 1024 + wv.get(k, 0.0) * w_scale * 1024
+            rec["bytes_per_launch"][g["gemm"]] = b
+            rec["detail"][g["gemm"]] = {"kernel": _short(k), "fetch_kib": fv[k],
+                                        "write_kib": wv.get(k, 0.0), "dispatches": fn[k],
+                                        "command_fetch": g["command_fetch"],
+                                        "command_write": g["command_write"]}
+            md.append(f"| {g['gemm']} | `{_short(k)}` | {fn[k]} | {fv[k]:.0f} | "
+                      f"{wv.get(k, 0.0):.0f} | {b:.4g} |")
+            md += ["", "    " + g["command_fetch"], "    " + g["command_write"], ""]
+        md.append(f"kernel sources: {rec['kernel_source']}")
+        with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        with open(os.path.join(out_dir, "traffic.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
 
 
 if __name__ == "__main__":
