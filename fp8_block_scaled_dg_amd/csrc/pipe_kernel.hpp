@@ -14,8 +14,10 @@
 // values of a lane then share one scale product per K-block, and the 32 columns
 // of a tile always sit in one 128-column sfB block.
 //
-// Operand movement: global memory -> LDS by direct-to-LDS DMA (global_load_lds,
-// 16 bytes per lane), no register staging. Three LDS stages hold K-blocks kb,
+// Operand movement: global memory -> LDS by direct-to-LDS buffer DMA (16 bytes per
+// lane), no register staging. Scales move once per three K-blocks, by 12-byte DMAs
+// per lane (three consecutive K-blocks of one row of sfA or sfB) into their own LDS
+// array. Three LDS stages hold K-blocks kb,
 // kb+1, kb+2; while block kb is multiplied, kb+1 and kb+2 are in flight. Each
 // stage is its own __shared__ array so that the compiler can tell a DMA into one
 // stage from a read of another; the K loop is unrolled by three so every stage
@@ -50,27 +52,31 @@ struct PipeCfg {
   static constexpr int TM = 2, TN = 2;                 // 32x32 tiles per wave (fixed)
   static constexpr int A_DMA = BM * kKBlock / 1024 / NW;  // 1 KB DMA instructions per wave
   static constexpr int B_DMA = BN * kKBlock / 1024 / NW;
-  static constexpr int RPW = BM / NW;                  // sfA rows loaded by one wave
-  static constexpr int NBT = BN / 128;                 // sfB blocks per tile
-  static constexpr int DMA_PER_KB = A_DMA + B_DMA + 2;  // + sfA + sfB
+  static constexpr int RPW = BM / NW;                  // sfA rows whose scales a wave loads
+  static constexpr int OPS_PER_KB = A_DMA + B_DMA;     // operand DMAs per K-block and wave
   static constexpr int OFF_B = BM * kKBlock;
-  static constexpr int OFF_SA = (BM + BN) * kKBlock;   // 256 bytes per wave
-  static constexpr int OFF_SB = OFF_SA + NW * 256;     // 256 bytes per wave
-  static constexpr int STAGE = OFF_SB + NW * 256;
+  static constexpr int STAGE = (BM + BN) * kKBlock;
   // M-tiles per raster group: 32 consecutive tiles cover 1024 A rows x 1024 B rows
   static constexpr int GROUP_M = 1024 / BM;
   static_assert(NW == 8, "two waves per SIMD");
   static_assert(BN % 128 == 0, "tile columns nest in 128-column scale blocks");
-  static_assert(A_DMA >= 1 && B_DMA >= 1 && RPW <= 64 && 64 % RPW == 0, "DMA split");
+  static_assert(A_DMA >= 1 && B_DMA >= 1 && RPW <= 32 && 32 % RPW == 0, "DMA split");
 };
 
-constexpr int kPipeStageBytes = 53248;  // (256 + 128) * 128 + 2 * 8 * 256
+constexpr int kPipeStageBytes = 49152;  // (256 + 128) * 128
 static_assert(PipeCfg<256, 128>::STAGE == kPipeStageBytes, "stage size");
 static_assert(PipeCfg<128, 256>::STAGE == kPipeStageBytes, "stage size");
 
 __shared__ __align__(16) uint8_t pipe_stage0[kPipeStageBytes];
 __shared__ __align__(16) uint8_t pipe_stage1[kPipeStageBytes];
 __shared__ __align__(16) uint8_t pipe_stage2[kPipeStageBytes];
+// Scales of three consecutive K-blocks. Lane l of wave w's 12-byte sfA DMA puts
+// row (w * RPW + l % RPW)'s three values at byte w * 1024 + 16 * l of pipe_scale.
+// Every wave's sfB DMA writes the same bytes to pipe_sfb: lane l holds the tile's
+// sfB row nb0 + min(l, BN/128 - 1) at byte 16 * l (identical concurrent writes).
+constexpr int kScaleWaveBytes = 1024;
+__shared__ __align__(16) uint8_t pipe_scale[8 * kScaleWaveBytes];
+__shared__ __align__(16) uint8_t pipe_sfb[1024];
 
 template <int S>
 __device__ __forceinline__ uint8_t* pipe_stage() {
@@ -108,23 +114,39 @@ __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, in
 
 // DMA sources of one thread: buffer resources for the tile's rows (wave-uniform,
 // SGPRs) plus 32-bit per-lane byte offsets; the K-block offset goes in the
-// instruction's scalar offset.
+// instruction's scalar offset. The scale resources end exactly at the end of sfA
+// and sfB, so reads past the last K-block of the last row return zero.
 template <class Cfg>
 struct PipeThread {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, sa_rsrc, sb_rsrc;
   uint32_t a_off[Cfg::A_DMA];
   uint32_t b_off[Cfg::B_DMA];
-  uint32_t sa_off, sb_off;
+  uint32_t sa_off;  // this lane's sfA row
+  uint32_t sb_off;  // this lane's sfB row
 };
 
-// Raw buffer over [p, p + 2^31): the offsets used stay below that.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
+// Raw buffer over [p, p + bytes), bytes < 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p,
+                                                           int64_t bytes = 0x7FFFFFFF) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0,
+                                           (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
+                                           0x00020000);
 }
 
-template <class Cfg, int S>
+// The DMAs of K-block kb into stage S. With SCALES (kb a multiple of 3) the batch
+// starts with the scales of K-blocks kb..kb+2 (the wave's share of sfA rows and its
+// copy of the tile's sfB rows) into pipe_scale. They go first, so that a wait that
+// leaves only the newest OPS_PER_KB operand DMAs in flight covers them too.
+template <class Cfg, int S, bool SCALES>
 __device__ __forceinline__ void pipe_issue(const PipeThread<Cfg>& th, int kb, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
+  if (SCALES) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sa_rsrc,
+                                             DG_LDS(pipe_scale + wave * kScaleWaveBytes), 12,
+                                             th.sa_off, kb * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sb_rsrc, DG_LDS(pipe_sfb), 12, th.sb_off, kb * 4,
+                                             0, 0);
+  }
   uint8_t* st = pipe_stage<S>();
   const int koff = kb * kKBlock;
 #pragma unroll
@@ -136,10 +158,6 @@ __device__ __forceinline__ void pipe_issue(const PipeThread<Cfg>& th, int kb, in
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         th.b_rsrc, DG_LDS(st + Cfg::OFF_B + (wave * Cfg::B_DMA + q) * 1024), 16, th.b_off[q], koff,
         0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sa_rsrc, DG_LDS(st + Cfg::OFF_SA + wave * 256), 4,
-                                           th.sa_off, kb * 4, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sb_rsrc, DG_LDS(st + Cfg::OFF_SB + wave * 256), 4,
-                                           th.sb_off, kb * 4, 0, 0);
 #endif
 }
 
@@ -182,7 +200,8 @@ __device__ __forceinline__ void promote8(v16f& acc, const v16f& p, float s) {
 template <class Cfg>
 struct PipeLane {
   uint32_t va[4], vb[4];
-  int sa0_idx, sa1_idx, sb_idx;
+  uint32_t sa0, sa1;  // byte offsets in pipe_scale of this lane's two A rows
+  uint32_t sb;        // byte offset in pipe_sfb of the wave's sfB row
   __device__ __forceinline__ PipeLane(int wave, int lane) {
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
     const int r32 = lane & 31, g = lane >> 5;
@@ -195,9 +214,9 @@ struct PipeLane {
       vb[k] = (uint32_t)Cfg::OFF_B + (uint32_t)(wn * 64 + r32) * kKBlock + c;
     }
     const int ra0 = wm * 64 + r32, ra1 = ra0 + 32;
-    sa0_idx = (ra0 / Cfg::RPW) * 64 + ra0 % Cfg::RPW;
-    sa1_idx = (ra1 / Cfg::RPW) * 64 + ra1 % Cfg::RPW;
-    sb_idx = wave * 64 + (wn * 64) / 128;
+    sa0 = (uint32_t)((ra0 / Cfg::RPW) * kScaleWaveBytes + (ra0 % Cfg::RPW) * 16);
+    sa1 = (uint32_t)((ra1 / Cfg::RPW) * kScaleWaveBytes + (ra1 % Cfg::RPW) * 16);
+    sb = (uint32_t)(((wn * 64) / 128) * 16);
   }
 };
 
@@ -215,6 +234,11 @@ struct Frag0 {
   v8i a0, a1, b0, b1;
 };
 
+// Scale products of the current three K-blocks for this lane's two A rows.
+struct PipeScales {
+  float s0[3], s1[3];
+};
+
 // One pipeline step for K-block kb held in stage S. On entry f holds the A-tile-0
 // and B-tile-0 fragments of kb (read during the previous step). Tiles are
 // multiplied in the order (0,0), (0,1), (1,0), (1,1), each as two chained MFMAs
@@ -228,16 +252,25 @@ struct Frag0 {
 template <class Cfg, int S>
 __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeLane<Cfg>& pl,
                                           v16f (&acc)[2][2], Frag0& f, v16f& carry,
-                                          float& carry_s, int kb, int KB, int wave) {
+                                          float& carry_s, PipeScales& sc, int kb, int KB,
+                                          int wave) {
   const uint8_t* st = read_base<S>();
   const uint8_t* nst = read_base<(S + 1) % 3>();
   const v16f zero = {};
 
   v8i b10, b11;
   read_tile(st, pl.vb, 1, b10, b11);
-  const float sb = ((const float*)(pipe_stage<S>() + Cfg::OFF_SB))[pl.sb_idx];
-  const float sa0 = ((const float*)(pipe_stage<S>() + Cfg::OFF_SA))[pl.sa0_idx];
-  const float sa1 = ((const float*)(pipe_stage<S>() + Cfg::OFF_SA))[pl.sa1_idx];
+  if (S == 0) {
+    // scales of K-blocks kb..kb+2 (landed before the previous barrier)
+    const v4f a0 = *(const v4f*)(pipe_scale + pl.sa0);
+    const v4f a1 = *(const v4f*)(pipe_scale + pl.sa1);
+    const v4f b = *(const v4f*)(pipe_sfb + pl.sb);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      sc.s0[j] = a0[j] * b[j];
+      sc.s1[j] = a1[j] * b[j];
+    }
+  }
   DG_FENCE();
   // tile (0,0) | carry
   v16f p = mfma32(f.b0, f.a0, zero);
@@ -248,7 +281,7 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   DG_FENCE();
   v8i a10, a11;
   read_tile(st, pl.va, 1, a10, a11);
-  const float s0 = sa0 * sb, s1 = sa1 * sb;
+  const float s0 = sc.s0[S], s1 = sc.s1[S];
   DG_FENCE();
   // tile (0,1) | (0,0)
   v16f q = mfma32(b10, f.a0, zero);
@@ -258,10 +291,10 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   promote8<8>(acc[0][0], p, s0);
   DG_FENCE();
   // block kb+1 in LDS, block kb's stage free
-  wait_vm_lgkm0<Cfg::DMA_PER_KB>();
+  wait_vm_lgkm0<Cfg::OPS_PER_KB>();
   __builtin_amdgcn_s_barrier();
   DG_FENCE();
-  pipe_issue<Cfg, S>(th, kb + 3 < KB ? kb + 3 : KB - 1, wave);
+  pipe_issue<Cfg, S, S == 0>(th, kb + 3 < KB ? kb + 3 : KB - 1, wave);
   DG_FENCE();
   read_tile(nst, pl.va, 0, f.a0, f.a1);
   DG_FENCE();
@@ -305,8 +338,8 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
   {
     th.a_rsrc = raw_rsrc(v.A + v.m0 * K);
     th.b_rsrc = raw_rsrc(v.B + v.n0 * K);
-    th.sa_rsrc = raw_rsrc(v.sfA + v.m0 * KB);
-    th.sb_rsrc = raw_rsrc(v.sfB + (int64_t)nb0 * KB);
+    th.sa_rsrc = raw_rsrc(v.sfA + v.m0 * KB, (v.rows - v.m0) * KB * 4);
+    th.sb_rsrc = raw_rsrc(v.sfB + (int64_t)nb0 * KB, (int64_t)(NB - nb0) * KB * 4);
     const int rsub = lane >> 3, c = lane & 7;
     const int a_rows = (int)(v.rows - v.m0 < Cfg::BM ? v.rows - v.m0 : Cfg::BM);
     const int b_rows = (int)(N - v.n0 < Cfg::BN ? N - v.n0 : Cfg::BN);
@@ -325,7 +358,7 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
     int arow = wave * Cfg::RPW + (lane % Cfg::RPW);
     if (arow >= a_rows) arow = a_rows - 1;
     th.sa_off = (uint32_t)arow * (uint32_t)KB * 4u;
-    int nb = lane < Cfg::NBT ? lane : Cfg::NBT - 1;
+    int nb = lane < Cfg::BN / 128 ? lane : Cfg::BN / 128 - 1;
     if (nb0 + nb >= NB) nb = NB - 1 - nb0;
     th.sb_off = (uint32_t)nb * (uint32_t)KB * 4u;
   }
@@ -339,28 +372,29 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
   float carry_s = 0.f;
   const PipeLane<Cfg> pl(wave, lane);
   Frag0 f;
+  PipeScales sc;
 
-  // prologue: blocks 0 and 1 in flight; once block 0 has landed everywhere, block
-  // 2 starts and the first fragments of block 0 are read
-  pipe_issue<Cfg, 0>(th, 0, wave);
-  pipe_issue<Cfg, 1>(th, KB > 1 ? 1 : KB - 1, wave);
+  // prologue: blocks 0 and 1 (and the scales of blocks 0..2) in flight; once block 0
+  // has landed everywhere, block 2 starts and the first fragments of block 0 are read
+  pipe_issue<Cfg, 0, true>(th, 0, wave);
+  pipe_issue<Cfg, 1, false>(th, KB > 1 ? 1 : KB - 1, wave);
   DG_FENCE();
-  wait_vm_lgkm0<Cfg::DMA_PER_KB>();
+  wait_vm_lgkm0<Cfg::OPS_PER_KB>();
   __builtin_amdgcn_s_barrier();
   DG_FENCE();
-  pipe_issue<Cfg, 2>(th, KB > 2 ? 2 : KB - 1, wave);
+  pipe_issue<Cfg, 2, false>(th, KB > 2 ? 2 : KB - 1, wave);
   DG_FENCE();
   read_tile(read_base<0>(), pl.va, 0, f.a0, f.a1);
   read_tile(read_base<0>(), pl.vb, 0, f.b0, f.b1);
   DG_FENCE();
   int kb = 0;
   for (; kb + 3 <= KB; kb += 3) {
-    pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, kb, KB, wave);
-    pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, kb + 1, KB, wave);
-    pipe_step<Cfg, 2>(th, pl, acc, f, carry, carry_s, kb + 2, KB, wave);
+    pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, sc, kb, KB, wave);
+    pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, sc, kb + 1, KB, wave);
+    pipe_step<Cfg, 2>(th, pl, acc, f, carry, carry_s, sc, kb + 2, KB, wave);
   }
-  if (kb < KB) pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, kb, KB, wave);
-  if (kb + 1 < KB) pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, kb + 1, KB, wave);
+  if (kb < KB) pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, sc, kb, KB, wave);
+  if (kb + 1 < KB) pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, sc, kb + 1, KB, wave);
   promote8<0>(acc[1][1], carry, carry_s);
   promote8<8>(acc[1][1], carry, carry_s);
   // every DMA has landed before the LDS can be reused or released
