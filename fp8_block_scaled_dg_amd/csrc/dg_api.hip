@@ -23,6 +23,7 @@
 #include "gemm_kernel.hpp"
 #include "pipe_kernel.hpp"
 #include "skinny_kernel.hpp"
+#include "stream_kernel.hpp"
 
 namespace dg {
 namespace {
@@ -176,13 +177,74 @@ dg_status launch_skinny(const Problem& p0, int64_t blocks, hipStream_t stream) {
   return DG_OK;
 }
 
+// ---------------------------------------------------------------- stream kernel
+
+// Split choice of the stream kernel: all splits of a column tile share an XCD, so an
+// XCD holds ceil(tiles / 8) tiles times S splits and should not exceed its 32 CUs.
+struct StreamPlan {
+  int64_t tiles, S, KS, grid;
+};
+
+template <class Cfg>
+StreamPlan stream_plan(int64_t N, int64_t K) {
+  StreamPlan pl;
+  const int64_t KB = K / kKBlock;
+  pl.tiles = (N + Cfg::BN - 1) / Cfg::BN;
+  const int64_t per_xcd = (pl.tiles + 7) / 8;
+  int64_t S = (kCUs / 8) / per_xcd;
+  if (S > Cfg::SMAX) S = Cfg::SMAX;
+  if (S > KB) S = KB;
+  if (S < 1) S = 1;
+  pl.KS = (KB + S - 1) / S;
+  pl.S = (KB + pl.KS - 1) / pl.KS;
+  pl.grid = 8 * per_xcd * pl.S;
+  return pl;
+}
+
+template <class Cfg>
+bool stream_fits(int64_t M, int64_t N, int64_t K) {
+  if (M > 64 || K / kKBlock < 1) return false;
+  return stream_plan<Cfg>(N, K).KS <= Cfg::D;
+}
+
+template <class Cfg>
+dg_status launch_stream(const Problem& p0, int64_t blocks, hipStream_t stream) {
+  (void)blocks;
+  const StreamPlan pl = stream_plan<Cfg>(p0.N, p0.K);
+  if (pl.KS > Cfg::D) return fail(DG_ERR_UNSUPPORTED_SHAPE, "K run %lld > %d", (long long)pl.KS, Cfg::D);
+  StreamArgs a{};
+  a.p = p0;
+  a.S = (int32_t)pl.S;
+  a.KS = (int32_t)pl.KS;
+  a.tiles = (int32_t)pl.tiles;
+  if (pl.grid > 0x7FFFFFFF) return fail(DG_ERR_UNSUPPORTED_SHAPE, "grid of %lld", (long long)pl.grid);
+  if (pl.S > 1) {
+    const size_t part = (size_t)(pl.tiles * pl.S) * 64 * Cfg::BN * sizeof(float);
+    dg_status st = get_workspace(stream, part, (size_t)pl.tiles, &a.ws, &a.counters);
+    if (st != DG_OK) return st;
+  }
+  hipLaunchKernelGGL((stream_kernel<Cfg>), dim3((unsigned)pl.grid), dim3(Cfg::NT), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
+  return DG_OK;
+}
+
+using Stream1x10 = StreamCfg<4, 1, 10>;
+using Stream2x4 = StreamCfg<4, 2, 4>;
+using Stream1x4 = StreamCfg<4, 1, 4>;
+using Stream8w10 = StreamCfg<8, 1, 10>;
+using Stream8w4 = StreamCfg<8, 1, 4>;
+using Stream2w4 = StreamCfg<2, 1, 4>;
+
 typedef dg_status (*Launcher)(const Problem&, int64_t, hipStream_t);
+typedef bool (*Fits)(int64_t M, int64_t N, int64_t K);
 
 struct CfgEntry {
   const char* name;
   Launcher dense, contiguous, masked;  // NULL where the configuration does not apply
   int max_m;                            // skinny: rows it covers; 0 = any
   int max_kb;                           // K/128 it supports; 0 = any
+  Fits fits;                            // further shape test (dense); NULL = none
 };
 
 // The pipelined kernel addresses a tile's rows with 32-bit offsets below 256 * K
@@ -206,6 +268,20 @@ const CfgEntry kTable[] = {
     {"skinny_w2_tn1_d5", launch_skinny<SkinnyCfg<2, 1, 5>>, nullptr, nullptr, 64, 0},
     {"skinny_w2_tn1_d8", launch_skinny<SkinnyCfg<2, 1, 8>>, nullptr, nullptr, 64, 0},
     {"skinny_w8_tn1_d4", launch_skinny<SkinnyCfg<8, 1, 4>>, nullptr, nullptr, 64, 0},
+    {"skinny_w8_tn1_d2", launch_skinny<SkinnyCfg<8, 1, 2>>, nullptr, nullptr, 64, 0},
+    {"skinny_w2_tn1_d2", launch_skinny<SkinnyCfg<2, 1, 2>>, nullptr, nullptr, 64, 0},
+    {"stream_w4_tn1_d10", launch_stream<Stream1x10>, nullptr, nullptr, 64, 0,
+     stream_fits<Stream1x10>},
+    {"stream_w4_tn2_d4", launch_stream<Stream2x4>, nullptr, nullptr, 64, 0,
+     stream_fits<Stream2x4>},
+    {"stream_w4_tn1_d4", launch_stream<Stream1x4>, nullptr, nullptr, 64, 0,
+     stream_fits<Stream1x4>},
+    {"stream_w8_tn1_d10", launch_stream<Stream8w10>, nullptr, nullptr, 64, 0,
+     stream_fits<Stream8w10>},
+    {"stream_w8_tn1_d4", launch_stream<Stream8w4>, nullptr, nullptr, 64, 0,
+     stream_fits<Stream8w4>},
+    {"stream_w2_tn1_d4", launch_stream<Stream2w4>, nullptr, nullptr, 64, 0,
+     stream_fits<Stream2w4>},
 };
 constexpr int kNumCfg = (int)(sizeof(kTable) / sizeof(kTable[0]));
 
@@ -220,11 +296,12 @@ Launcher launcher_for(int id, int kind) {
   return kind == kDense ? c.dense : kind == kContiguous ? c.contiguous : c.masked;
 }
 
-bool cfg_applies(int id, int kind, int64_t M, int64_t K) {
+bool cfg_applies(int id, int kind, int64_t M, int64_t N, int64_t K) {
   const CfgEntry& c = kTable[id];
   if (!launcher_for(id, kind)) return false;
   if (c.max_m && M > c.max_m) return false;
   if (c.max_kb && K / kKBlock > c.max_kb) return false;
+  if (c.fits && !c.fits(M, N, K)) return false;
   return true;
 }
 
@@ -235,10 +312,15 @@ int select_config(int kind, int64_t m, int64_t M, int64_t n, int64_t k, int32_t 
   const char* forced = getenv("DG_FORCE_CONFIG");
   if (forced && *forced) {
     const int id = find_cfg(forced);
-    if (id >= 0 && cfg_applies(id, kind, M, k)) return id;
+    if (id >= 0 && cfg_applies(id, kind, M, n, k)) return id;
   }
   if (kind == kDense && M <= 64) {
-    // the launcher's split choice for 64-column tiles decides the pipeline depth:
+    // long K: the stream kernel (every load of a K run issued at once, split-K
+    // reduction) when its run fits; short K: the rolling skinny kernel (measured
+    // faster when each workgroup holds only a few K-blocks)
+    const int s1 = find_cfg("stream_w4_tn1_d10");
+    if (k / kKBlock >= 16 && cfg_applies(s1, kind, M, n, k)) return s1;
+    // otherwise the rolling skinny kernel; its split choice for 64-column tiles decides the pipeline depth:
     // long K runs per workgroup keep 8 blocks in flight, short ones 2
     const int64_t kb = k / kKBlock, tiles = (n + 63) / 64;
     int64_t s = kCUs / tiles;
