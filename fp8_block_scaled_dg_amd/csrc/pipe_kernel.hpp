@@ -229,9 +229,10 @@ __device__ __forceinline__ void read_tile(const uint8_t* st, const uint32_t (&v)
   h1 = frag_at(p, v[2], v[3]);
 }
 
-// Fragments of A tile 0 and B tile 0 of a K-block: read one step ahead.
+// Fragments a K-block's step starts with: A tile 0 and both B tiles, read during
+// the previous step.
 struct Frag0 {
-  v8i a0, a1, b0, b1;
+  v8i a0, a1, b0, b1, c0, c1;  // A tile 0 (K halves), B tile 0, B tile 1
 };
 
 // Scale products of the current three K-blocks for this lane's two A rows.
@@ -239,56 +240,52 @@ struct PipeScales {
   float s0[3], s1[3];
 };
 
-// One pipeline step for K-block kb held in stage S. On entry f holds the A-tile-0
-// and B-tile-0 fragments of kb (read during the previous step). Tiles are
-// multiplied in the order (0,0), (0,1), (1,0), (1,1), each as two chained MFMAs
-// (K halves); each tile's promotion runs in the shadow of the next tile's MFMAs and
-// the last tile's partial (carry) is promoted during the next step's first tile.
-// Halfway, once A tile 0 of kb is dead, the wave waits for its own DMAs of block
-// kb+1 and meets the others at the barrier: block kb+1 is then in LDS and every
-// read of block kb is done, so the DMA of block kb+3 refills kb's stage and the
-// fragments of kb+1 are read into the registers kb no longer needs.
-// Scheduling fences keep this order; the compiler inserts only the LDS waits.
+// One pipeline step for K-block kb held in stage S.
+// MFMA order: independent pairs, so a tile's second K half never waits on its first:
+//   M1 t00.h0  M2 t01.h0  M3 t00.h1  M4 t01.h1  M5 t10.h0  M6 t11.h0  M7 t10.h1  M8 t11.h1
+// (tij = A tile i x B tile j). Each tile's promotion runs in the shadow of the two
+// MFMAs after its last one: t00 and t01 during M5-M8, t10 and t11 of block kb during
+// M1-M4 of the next step (carries c10, c11).
+// After M4, A tile 0 of kb is dead: the wave waits for its own DMAs of block kb+1
+// and meets the others at the barrier; block kb+1 is then in LDS and every read of
+// block kb is done, so the DMA of block kb+3 refills kb's stage, and A tile 0 and
+// B tile 1 of kb+1 are read (B tile 1 into spare registers). B tile 0 of kb+1 is
+// read after M7, when kb's is dead. Scheduling fences keep this order; the compiler
+// inserts only the LDS waits.
 template <class Cfg, int S>
 __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeLane<Cfg>& pl,
-                                          v16f (&acc)[2][2], Frag0& f, v16f& carry,
+                                          v16f (&acc)[2][2], Frag0& f, v16f (&carry)[2],
                                           float& carry_s, PipeScales& sc, int kb, int KB,
                                           int wave) {
   const uint8_t* st = read_base<S>();
   const uint8_t* nst = read_base<(S + 1) % 3>();
   const v16f zero = {};
 
-  v8i b10, b11;
-  read_tile(st, pl.vb, 1, b10, b11);
+  v8i a10, a11;
+  read_tile(st, pl.va, 1, a10, a11);
   if (S == 0) {
     // scales of K-blocks kb..kb+2 (landed before the previous barrier)
-    const v4f a0 = *(const v4f*)(pipe_scale + pl.sa0);
-    const v4f a1 = *(const v4f*)(pipe_scale + pl.sa1);
+    const v4f x0 = *(const v4f*)(pipe_scale + pl.sa0);
+    const v4f x1 = *(const v4f*)(pipe_scale + pl.sa1);
     const v4f b = *(const v4f*)(pipe_sfb + pl.sb);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      sc.s0[j] = a0[j] * b[j];
-      sc.s1[j] = a1[j] * b[j];
+      sc.s0[j] = x0[j] * b[j];
+      sc.s1[j] = x1[j] * b[j];
     }
   }
   DG_FENCE();
-  // tile (0,0) | carry
-  v16f p = mfma32(f.b0, f.a0, zero);
-  promote8<0>(acc[1][1], carry, carry_s);
+  v16f p00 = mfma32(f.b0, f.a0, zero);  // M1
+  promote8<0>(acc[1][0], carry[0], carry_s);
   DG_FENCE();
-  p = mfma32(f.b1, f.a1, p);
-  promote8<8>(acc[1][1], carry, carry_s);
+  v16f p01 = mfma32(f.c0, f.a0, zero);  // M2
+  promote8<8>(acc[1][0], carry[0], carry_s);
   DG_FENCE();
-  v8i a10, a11;
-  read_tile(st, pl.va, 1, a10, a11);
-  const float s0 = sc.s0[S], s1 = sc.s1[S];
+  p00 = mfma32(f.b1, f.a1, p00);  // M3
+  promote8<0>(acc[1][1], carry[1], carry_s);
   DG_FENCE();
-  // tile (0,1) | (0,0)
-  v16f q = mfma32(b10, f.a0, zero);
-  promote8<0>(acc[0][0], p, s0);
-  DG_FENCE();
-  q = mfma32(b11, f.a1, q);
-  promote8<8>(acc[0][0], p, s0);
+  p01 = mfma32(f.c1, f.a1, p01);  // M4
+  promote8<8>(acc[1][1], carry[1], carry_s);
   DG_FENCE();
   // block kb+1 in LDS, block kb's stage free
   wait_vm_lgkm0<Cfg::OPS_PER_KB>();
@@ -296,25 +293,29 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   DG_FENCE();
   pipe_issue<Cfg, S, S == 0>(th, kb + 3 < KB ? kb + 3 : KB - 1, wave);
   DG_FENCE();
+  const float s0 = sc.s0[S], s1 = sc.s1[S];
   read_tile(nst, pl.va, 0, f.a0, f.a1);
+  v8i c0n, c1n;
+  read_tile(nst, pl.vb, 1, c0n, c1n);
   DG_FENCE();
-  // tile (1,0) | (0,1)
-  v16f r = mfma32(f.b0, a10, zero);
-  promote8<0>(acc[0][1], q, s0);
+  v16f p10 = mfma32(f.b0, a10, zero);  // M5
+  promote8<0>(acc[0][0], p00, s0);
   DG_FENCE();
-  r = mfma32(f.b1, a11, r);
-  promote8<8>(acc[0][1], q, s0);
+  v16f p11 = mfma32(f.c0, a10, zero);  // M6
+  promote8<8>(acc[0][0], p00, s0);
+  DG_FENCE();
+  p10 = mfma32(f.b1, a11, p10);  // M7
+  promote8<0>(acc[0][1], p01, s0);
   DG_FENCE();
   read_tile(nst, pl.vb, 0, f.b0, f.b1);
   DG_FENCE();
-  // tile (1,1) | (1,0)
-  v16f t = mfma32(b10, a10, zero);
-  promote8<0>(acc[1][0], r, s1);
+  p11 = mfma32(f.c1, a11, p11);  // M8
+  promote8<8>(acc[0][1], p01, s0);
   DG_FENCE();
-  t = mfma32(b11, a11, t);
-  promote8<8>(acc[1][0], r, s1);
-  DG_FENCE();
-  carry = t;
+  f.c0 = c0n;
+  f.c1 = c1n;
+  carry[0] = p10;
+  carry[1] = p11;
   carry_s = s1;
 }
 
@@ -368,7 +369,7 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
-  v16f carry = {};
+  v16f carry[2] = {v16f{}, v16f{}};
   float carry_s = 0.f;
   const PipeLane<Cfg> pl(wave, lane);
   Frag0 f;
@@ -386,6 +387,7 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
   DG_FENCE();
   read_tile(read_base<0>(), pl.va, 0, f.a0, f.a1);
   read_tile(read_base<0>(), pl.vb, 0, f.b0, f.b1);
+  read_tile(read_base<0>(), pl.vb, 1, f.c0, f.c1);
   DG_FENCE();
   int kb = 0;
   for (; kb + 3 <= KB; kb += 3) {
@@ -395,8 +397,10 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
   }
   if (kb < KB) pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, sc, kb, KB, wave);
   if (kb + 1 < KB) pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, sc, kb + 1, KB, wave);
-  promote8<0>(acc[1][1], carry, carry_s);
-  promote8<8>(acc[1][1], carry, carry_s);
+  promote8<0>(acc[1][0], carry[0], carry_s);
+  promote8<8>(acc[1][0], carry[0], carry_s);
+  promote8<0>(acc[1][1], carry[1], carry_s);
+  promote8<8>(acc[1][1], carry[1], carry_s);
   // every DMA has landed before the LDS can be reused or released
   DG_FENCE();
   __builtin_amdgcn_s_waitcnt(0);
