@@ -68,15 +68,54 @@ dg_status launch_tile(const Problem& p0, int64_t blocks, hipStream_t stream) {
   return DG_OK;
 }
 
+dg_status get_workspace(hipStream_t stream, size_t partial_bytes, size_t counters,
+                        float** partials, uint32_t** counter_ptr);
+
+// Dense tail balancing: with T tiles on kCUs CUs (one workgroup each), the last
+// r = T mod kCUs tiles would run in a partial round. Each of them is split into
+// `parts` K ranges (at least 8 K-blocks each) so that the last round fills the GPU.
+struct TailSplit {
+  int64_t full, parts;
+};
+
+TailSplit pipe_tail_split(int64_t tiles, int64_t KB) {
+  TailSplit t{tiles, 1};
+  const int64_t r = tiles % kCUs;
+  if (r == 0) return t;
+  int64_t parts = kCUs / r;
+  if (parts > 8) parts = 8;
+  if (parts > KB / 8) parts = KB / 8;
+  if (parts < 2) return t;
+  t.full = tiles - r;
+  t.parts = parts;
+  return t;
+}
+
 template <class Cfg, int KIND>
 dg_status launch_pipe(const Problem& p0, int64_t blocks, hipStream_t stream) {
-  Problem p = p0;
+  PipeArgs a{};
+  a.p = p0;
+  Problem& p = a.p;
   p.tiles_m = (int32_t)((p.M + Cfg::BM - 1) / Cfg::BM);
   p.tiles_n = (int32_t)((p.N + Cfg::BN - 1) / Cfg::BN);
-  const int64_t grid = blocks * p.tiles_m * p.tiles_n;
+  int64_t grid = blocks * p.tiles_m * p.tiles_n;
   if (grid <= 0) return DG_OK;
   if (grid > 0x7FFFFFFF) return fail(DG_ERR_UNSUPPORTED_SHAPE, "grid of %lld tiles", (long long)grid);
-  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream, p);
+  a.full_tiles = (int32_t)grid;
+  a.parts = 1;
+  if (KIND == kDense) {
+    const TailSplit ts = pipe_tail_split(grid, p.K / kKBlock);
+    if (ts.parts > 1) {
+      const int64_t split = grid - ts.full;
+      const size_t bytes = (size_t)(split * ts.parts) * Cfg::BM * Cfg::BN * sizeof(float);
+      dg_status st = get_workspace(stream, bytes, (size_t)split, &a.ws, &a.counters);
+      if (st != DG_OK) return st;
+      a.full_tiles = (int32_t)ts.full;
+      a.parts = (int32_t)ts.parts;
+      grid = ts.full + split * ts.parts;
+    }
+  }
+  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
   return DG_OK;

@@ -319,12 +319,12 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   carry_s = s1;
 }
 
-// Multiplies one tile: rows [m0, m0+BM) of the view, columns [n0, n0+BN).
-// valid_rows bounds the rows that are stored; for the contiguous layout only rows
-// whose m_indices entry equals `expert` are stored.
-template <class Cfg, int KIND>
-__device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, int expert,
-                                          int valid_rows) {
+// Multiplies rows [m0, m0+BM) of the view by columns [n0, n0+BN) over the K-blocks
+// [kb_lo, kb_hi) and leaves the fp32 tile in acc (lane layout: row lane % 32 of each
+// 32x32 tile, columns 8*(e/4) + 4*(lane/32) + e%4).
+template <class Cfg>
+__device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& v, int kb_lo,
+                                              int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN]) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR addresses
@@ -364,7 +364,6 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
     th.sb_off = (uint32_t)nb * (uint32_t)KB * 4u;
   }
 
-  v16f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -377,26 +376,26 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
 
   // prologue: blocks 0 and 1 (and the scales of blocks 0..2) in flight; once block 0
   // has landed everywhere, block 2 starts and the first fragments of block 0 are read
-  pipe_issue<Cfg, 0, true>(th, 0, wave);
-  pipe_issue<Cfg, 1, false>(th, KB > 1 ? 1 : KB - 1, wave);
+  pipe_issue<Cfg, 0, true>(th, kb_lo, wave);
+  pipe_issue<Cfg, 1, false>(th, kb_lo + 1 < kb_hi ? kb_lo + 1 : kb_hi - 1, wave);
   DG_FENCE();
   wait_vm_lgkm0<Cfg::OPS_PER_KB>();
   __builtin_amdgcn_s_barrier();
   DG_FENCE();
-  pipe_issue<Cfg, 2, false>(th, KB > 2 ? 2 : KB - 1, wave);
+  pipe_issue<Cfg, 2, false>(th, kb_lo + 2 < kb_hi ? kb_lo + 2 : kb_hi - 1, wave);
   DG_FENCE();
   read_tile(read_base<0>(), pl.va, 0, f.a0, f.a1);
   read_tile(read_base<0>(), pl.vb, 0, f.b0, f.b1);
   read_tile(read_base<0>(), pl.vb, 1, f.c0, f.c1);
   DG_FENCE();
-  int kb = 0;
-  for (; kb + 3 <= KB; kb += 3) {
-    pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, sc, kb, KB, wave);
-    pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, sc, kb + 1, KB, wave);
-    pipe_step<Cfg, 2>(th, pl, acc, f, carry, carry_s, sc, kb + 2, KB, wave);
+  int kb = kb_lo;
+  for (; kb + 3 <= kb_hi; kb += 3) {
+    pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
+    pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
+    pipe_step<Cfg, 2>(th, pl, acc, f, carry, carry_s, sc, kb + 2, kb_hi, wave);
   }
-  if (kb < KB) pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, sc, kb, KB, wave);
-  if (kb + 1 < KB) pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, sc, kb + 1, KB, wave);
+  if (kb < kb_hi) pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
+  if (kb + 1 < kb_hi) pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
   promote8<0>(acc[1][0], carry[0], carry_s);
   promote8<8>(acc[1][0], carry[0], carry_s);
   promote8<0>(acc[1][1], carry[1], carry_s);
@@ -406,9 +405,17 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   DG_FENCE();
+}
 
-  // ---- epilogue: bf16 RNE; lane holds row (lane % 32) of each 32x32 tile and
-  // columns 8*(e/4) + 4*(lane/32) + e%4
+// bf16 RNE store of a finished tile: produced rows (< valid_rows, and for the
+// contiguous layout only rows whose m_indices entry equals `expert`) and in-range
+// columns only.
+template <class Cfg, int KIND>
+__device__ __forceinline__ void pipe_store(const Problem& p, const TileView& v, int expert,
+                                           int valid_rows, const v16f (&acc)[Cfg::TM][Cfg::TN]) {
+  constexpr int TM = Cfg::TM, TN = Cfg::TN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t N = p.N;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int r32 = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -436,8 +443,117 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
 }
 
 template <class Cfg, int KIND>
-__global__ void __launch_bounds__(Cfg::NT) pipe_kernel(Problem p) {
-  const int t = xcd_tile_order(blockIdx.x, gridDim.x);
+__device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, int expert,
+                                          int valid_rows) {
+  v16f acc[Cfg::TM][Cfg::TN];
+  pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc);
+  pipe_store<Cfg, KIND>(p, v, expert, valid_rows, acc);
+}
+
+struct PipeArgs {
+  Problem p;
+  float* ws;           // split tail: [tile][part][BM * BN] fp32 partials
+  uint32_t* counters;  // split tail: one per tile, zero between calls
+  int32_t full_tiles;  // dense: tiles computed whole (the first of the tile order)
+  int32_t parts;       // dense: K parts of each remaining tile
+};
+
+// Dense tail tile: K-blocks [kb_lo, kb_hi) of tile `tt` (index among the split
+// tiles), part `part` of `parts`. Each part writes its fp32 tile with device-scope
+// stores and counts its arrival; the last part to arrive adds the parts in part
+// order -- a fixed order, so the result is deterministic -- and stores bf16.
+template <class Cfg>
+__device__ __forceinline__ void pipe_split_tile(const PipeArgs& a, const TileView& v, int tt,
+                                                int part, int kb_lo, int kb_hi) {
+  constexpr int TM = Cfg::TM, TN = Cfg::TN, BMN = Cfg::BM * Cfg::BN;
+  v16f acc[TM][TN];
+  pipe_mainloop<Cfg>(a.p, v, kb_lo, kb_hi, acc);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
+      a.ws + (int64_t)tt * a.parts * BMN, 0, 0x7FFFFFFF, 0x00020000);
+  constexpr int kSc1 = 16;  // device scope: the parts run on different XCDs
+  auto off = [&](int pt, int i, int j, int q) {
+    return (uint32_t)(pt * BMN * 4 + ((((wave * TM + i) * TN + j) * 4 + q) * 64 + lane) * 16);
+  };
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v4u{__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])},
+            ws, off(part, i, j, q), 0, kSc1);
+  __builtin_amdgcn_s_waitcnt(0);  // the partial has reached memory
+  __builtin_amdgcn_s_barrier();
+  __shared__ uint32_t s_last;
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&a.counters[tt], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(a.parts - 1);
+  __syncthreads();
+  if (!s_last) return;
+  v16f sum[TM][TN];
+  for (int pt = 0; pt < a.parts; ++pt) {
+    v16f x[TM][TN];
+    if (pt == part) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) x[i][j] = acc[i][j];
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v4u u = __builtin_amdgcn_raw_buffer_load_b128(ws, off(pt, i, j, q), 0, kSc1);
+            x[i][j][4 * q] = __uint_as_float(u[0]);
+            x[i][j][4 * q + 1] = __uint_as_float(u[1]);
+            x[i][j][4 * q + 2] = __uint_as_float(u[2]);
+            x[i][j][4 * q + 3] = __uint_as_float(u[3]);
+          }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if (pt == 0) {
+          sum[i][j] = x[i][j];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sum[i][j][e] += x[i][j][e];
+        }
+      }
+  }
+  if (tid == 0)
+    __hip_atomic_store(&a.counters[tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  pipe_store<Cfg, kDense>(a.p, v, 0, (int)a.p.M, sum);
+}
+
+template <class Cfg, int KIND>
+__global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
+  const Problem& p = args.p;
+  if (KIND == kDense && (int)blockIdx.x >= args.full_tiles) {
+    const int h = (int)blockIdx.x - args.full_tiles;
+    const int tt = h / args.parts, part = h - tt * args.parts;
+    int tm, tn;
+    grouped_tile<Cfg::GROUP_M>(args.full_tiles + tt, p.tiles_m, p.tiles_n, tm, tn);
+    const int KB = (int)(p.K / kKBlock);
+    TileView v;
+    v.m0 = (int64_t)tm * Cfg::BM;
+    v.n0 = (int64_t)tn * Cfg::BN;
+    v.A = p.A;
+    v.sfA = p.sfA;
+    v.C = p.C;
+    v.rows = p.M;
+    v.B = p.B;
+    v.sfB = p.sfB;
+    pipe_split_tile<Cfg>(args, v, tt, part, part * KB / args.parts, (part + 1) * KB / args.parts);
+    return;
+  }
+  const int t = xcd_tile_order(blockIdx.x, KIND == kDense ? args.full_tiles : gridDim.x);
   const int NB = (int)((p.N + kKBlock - 1) / kKBlock);
   const int KB = (int)(p.K / kKBlock);
   TileView v;

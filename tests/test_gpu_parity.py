@@ -92,6 +92,27 @@ def test_dense_integer_exact_bitwise(M, N, K):
     assert_bitwise(g, oracle.gemm_nt(A, B, sfA, sfB), what=f"int {M}x{N}x{K}")
 
 
+# Tile counts that leave a partial last round on 256 CUs, with K long enough that the
+# compute-bound kernel splits the tail tiles into 2, 4 and 8 K parts (whose partials
+# are added by the last part to arrive). Integer-valued inputs keep every partial sum
+# exact, so the split must not change a single bit.
+@pytest.mark.parametrize("M,N,K", [(384, 768, 2048), (256, 1280, 4096), (128, 512, 8192),
+                                   (300, 704, 3072)])
+def test_dense_tail_split_integer_exact_bitwise(M, N, K):
+    rng = np.random.default_rng(M * 5 + N + K * 3)
+    A, B, sfA, sfB = int_operands(rng, M, N, K)
+    g = run_dense(A, B, sfA, sfB)
+    assert_bitwise(g, oracle.gemm_nt(A, B, sfA, sfB), what=f"tail int {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(384, 768, 2048), (256, 1280, 4096)])
+def test_dense_tail_split_gaussian(M, N, K):
+    w = synth.dense(M, N, K, seed_base=888000 + M)
+    g = run_dense(w.A, w.B, w.sfA, w.sfB)
+    rep = assert_parity(g, oracle.gemm_nt(w.A, w.B, w.sfA, w.sfB), what=f"tail {M}x{N}x{K}")
+    print(f"tail {M}x{N}x{K}:", rep)
+
+
 @pytest.mark.parametrize("M,N,K", [(65, 2112, 1024), (300, 528, 640), (1, 32, 128), (17, 4096, 256),
                                    (64, 2112, 1664), (33, 7168, 2048)])
 def test_dense_gaussian_shapes(M, N, K):
