@@ -10,7 +10,9 @@ article's benchmark table, section 2.1); the metric is achieved algorithmic HBM
 throughput in GB/s. Other workloads (--workload prefill | moe_cont | moe_mask |
 small) report TFLOPS against the dense FP8 MFMA peak.
 
-Timing: W untimed warmup steps, then exactly K steps between two synchronisations.
+Timing: W untimed warmup steps (more if they take under --warmup-seconds, so that
+the clocks have ramped up from idle; the JSON reports the count run), then exactly
+K steps between two synchronisations.
 The K launches of each GEMM run back to back between a pair of HIP events
 (torch.cuda.Event, on the stream the kernels are launched on), which gives each
 kernel's average launch duration. Input and output buffers rotate over enough
@@ -188,6 +190,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="keep running untimed warmup steps past --warmup until this much "
+                         "time has passed, so that the GPU clocks have left their idle state")
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -230,10 +235,16 @@ def main():
         g.upload(copies)
     torch.cuda.synchronize()
 
-    for s in range(args.warmup):
-        for g in gemms:
-            g.launch(s)
-    torch.cuda.synchronize()
+    warm = 0
+    t0 = time.perf_counter()
+    while warm < args.warmup or time.perf_counter() - t0 < args.warmup_seconds:
+        chunk = max(1, args.warmup - warm) if warm < args.warmup else max(1, warm)
+        for s in range(warm, warm + chunk):
+            for g in gemms:
+                g.launch(s)
+        warm += chunk
+        torch.cuda.synchronize()
+    args.warmup = warm  # the number of untimed steps actually run
 
     # Timed region: the K steps' launches, grouped by GEMM (all K launches of one GEMM
     # back to back on rotating buffers, then the next GEMM), bracketed by events on

@@ -252,11 +252,20 @@ struct PipeScales {
 // B tile 1 of kb+1 are read (B tile 1 into spare registers). B tile 0 of kb+1 is
 // read after M7, when kb's is dead. Scheduling fences keep this order; the compiler
 // inserts only the LDS waits.
-template <class Cfg, int S>
+template <class Cfg, int S, bool ACT>
 __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeLane<Cfg>& pl,
                                           v16f (&acc)[2][2], Frag0& f, v16f (&carry)[2],
                                           float& carry_s, PipeScales& sc, int kb, int KB,
                                           int wave) {
+  if constexpr (!ACT) {
+    // a wave with no output rows or columns of its own: only its share of the DMAs
+    wait_vm_lgkm0<Cfg::OPS_PER_KB>();
+    __builtin_amdgcn_s_barrier();
+    DG_FENCE();
+    pipe_issue<Cfg, S, S == 0>(th, kb + 3 < KB ? kb + 3 : KB - 1, wave);
+    DG_FENCE();
+    return;
+  }
   const uint8_t* st = read_base<S>();
   const uint8_t* nst = read_base<(S + 1) % 3>();
   const v16f zero = {};
@@ -321,10 +330,13 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
 
 // Multiplies rows [m0, m0+BM) of the view by columns [n0, n0+BN) over the K-blocks
 // [kb_lo, kb_hi) and leaves the fp32 tile in acc (lane layout: row lane % 32 of each
-// 32x32 tile, columns 8*(e/4) + 4*(lane/32) + e%4).
-template <class Cfg>
-__device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& v, int kb_lo,
-                                              int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN]) {
+// 32x32 tile, columns 8*(e/4) + 4*(lane/32) + e%4). Rows at or past v.rows and
+// columns at or past N read as zero (the buffer resources end there). With ACT false
+// the wave only moves its share of the tile's operands and leaves acc at zero: the
+// caller passes false to a wave whose 64 x 64 sub-tile holds nothing to store.
+template <class Cfg, bool ACT>
+__device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileView& v, int kb_lo,
+                                                 int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN]) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR addresses
@@ -337,24 +349,24 @@ __device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& 
   // the host checks that this stays below 2^31.
   PipeThread<Cfg> th;
   {
-    th.a_rsrc = raw_rsrc(v.A + v.m0 * K);
-    th.b_rsrc = raw_rsrc(v.B + v.n0 * K);
+    const int a_rows = (int)(v.rows - v.m0 < Cfg::BM ? v.rows - v.m0 : Cfg::BM);
+    const int b_rows = (int)(N - v.n0 < Cfg::BN ? N - v.n0 : Cfg::BN);
+    // rows past the ends are out of the resources' range: the DMA writes zeros and
+    // fetches nothing
+    th.a_rsrc = raw_rsrc(v.A + v.m0 * K, (int64_t)a_rows * K);
+    th.b_rsrc = raw_rsrc(v.B + v.n0 * K, (int64_t)b_rows * K);
     th.sa_rsrc = raw_rsrc(v.sfA + v.m0 * KB, (v.rows - v.m0) * KB * 4);
     th.sb_rsrc = raw_rsrc(v.sfB + (int64_t)nb0 * KB, (int64_t)(NB - nb0) * KB * 4);
     const int rsub = lane >> 3, c = lane & 7;
-    const int a_rows = (int)(v.rows - v.m0 < Cfg::BM ? v.rows - v.m0 : Cfg::BM);
-    const int b_rows = (int)(N - v.n0 < Cfg::BN ? N - v.n0 : Cfg::BN);
 #pragma unroll
     for (int q = 0; q < Cfg::A_DMA; ++q) {
       const int R = (wave * Cfg::A_DMA + q) * 8 + rsub;
-      const int row = R < a_rows ? R : a_rows - 1;
-      th.a_off[q] = (uint32_t)row * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+      th.a_off[q] = (uint32_t)R * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
     }
 #pragma unroll
     for (int q = 0; q < Cfg::B_DMA; ++q) {
       const int R = (wave * Cfg::B_DMA + q) * 8 + rsub;
-      const int row = R < b_rows ? R : b_rows - 1;
-      th.b_off[q] = (uint32_t)row * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+      th.b_off[q] = (uint32_t)R * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
     }
     int arow = wave * Cfg::RPW + (lane % Cfg::RPW);
     if (arow >= a_rows) arow = a_rows - 1;
@@ -384,27 +396,48 @@ __device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& 
   DG_FENCE();
   pipe_issue<Cfg, 2, false>(th, kb_lo + 2 < kb_hi ? kb_lo + 2 : kb_hi - 1, wave);
   DG_FENCE();
-  read_tile(read_base<0>(), pl.va, 0, f.a0, f.a1);
-  read_tile(read_base<0>(), pl.vb, 0, f.b0, f.b1);
-  read_tile(read_base<0>(), pl.vb, 1, f.c0, f.c1);
+  if (ACT) {
+    read_tile(read_base<0>(), pl.va, 0, f.a0, f.a1);
+    read_tile(read_base<0>(), pl.vb, 0, f.b0, f.b1);
+    read_tile(read_base<0>(), pl.vb, 1, f.c0, f.c1);
+  }
   DG_FENCE();
   int kb = kb_lo;
   for (; kb + 3 <= kb_hi; kb += 3) {
-    pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
-    pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
-    pipe_step<Cfg, 2>(th, pl, acc, f, carry, carry_s, sc, kb + 2, kb_hi, wave);
+    pipe_step<Cfg, 0, ACT>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
+    pipe_step<Cfg, 1, ACT>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
+    pipe_step<Cfg, 2, ACT>(th, pl, acc, f, carry, carry_s, sc, kb + 2, kb_hi, wave);
   }
-  if (kb < kb_hi) pipe_step<Cfg, 0>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
-  if (kb + 1 < kb_hi) pipe_step<Cfg, 1>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
-  promote8<0>(acc[1][0], carry[0], carry_s);
-  promote8<8>(acc[1][0], carry[0], carry_s);
-  promote8<0>(acc[1][1], carry[1], carry_s);
-  promote8<8>(acc[1][1], carry[1], carry_s);
+  if (kb < kb_hi) pipe_step<Cfg, 0, ACT>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
+  if (kb + 1 < kb_hi)
+    pipe_step<Cfg, 1, ACT>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
+  if (ACT) {
+    promote8<0>(acc[1][0], carry[0], carry_s);
+    promote8<8>(acc[1][0], carry[0], carry_s);
+    promote8<0>(acc[1][1], carry[1], carry_s);
+    promote8<8>(acc[1][1], carry[1], carry_s);
+  }
   // every DMA has landed before the LDS can be reused or released
   DG_FENCE();
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   DG_FENCE();
+}
+
+// The wave's sub-tile holds output when its first row is below v.rows and its first
+// column below N; `any_row` lets the caller rule out sub-tiles whose rows are all
+// someone else's (contiguous layout). Both branches pass the same barriers.
+template <class Cfg>
+__device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& v, int kb_lo,
+                                              int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN],
+                                              bool any_row = true) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const bool act = any_row && v.m0 + wm * 64 < v.rows && v.n0 + wn * 64 < p.N;
+  if (act)
+    pipe_mainloop_as<Cfg, true>(p, v, kb_lo, kb_hi, acc);
+  else
+    pipe_mainloop_as<Cfg, false>(p, v, kb_lo, kb_hi, acc);
 }
 
 // bf16 RNE store of a finished tile: produced rows (< valid_rows, and for the
@@ -444,10 +477,66 @@ __device__ __forceinline__ void pipe_store(const Problem& p, const TileView& v, 
 
 template <class Cfg, int KIND>
 __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, int expert,
-                                          int valid_rows) {
+                                          int valid_rows, bool any_row = true) {
   v16f acc[Cfg::TM][Cfg::TN];
-  pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc);
+  pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, any_row);
   pipe_store<Cfg, KIND>(p, v, expert, valid_rows, acc);
+}
+
+// Masked layout: live tile `b` of the schedule that lists, expert by expert, the
+// ceil(valid_e / BM) x tiles_n tiles of each expert (valid_e = masked_m[e] clamped to
+// [0, M]). Workgroups are numbered in that order through xcd_tile_order, so each XCD
+// gets an equal contiguous share of the live tiles; expert = -1 past the live count.
+// Every lane of every wave computes the same values (wave-wide scans over 64
+// experts at a time).
+struct MaskedTile {
+  int expert, valid, local;
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+template <int BM>
+__device__ __forceinline__ MaskedTile masked_tile(const int32_t* masked_m, int G, int M,
+                                                  int tiles_n, int b) {
+  const int lane = threadIdx.x & 63;
+  auto count = [&](int e, int& valid) {
+    int v = e < G ? masked_m[e] : 0;
+    v = v < 0 ? 0 : (v > M ? M : v);
+    valid = v;
+    return (v + BM - 1) / BM * tiles_n;
+  };
+  int live = 0;
+  for (int e0 = 0; e0 < G; e0 += 64) {
+    int valid;
+    const int incl = wave_incl_scan(count(e0 + lane, valid), lane);
+    live += __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+  }
+  MaskedTile r{-1, 0, 0};
+  if (b >= live) return r;
+  const int t = xcd_tile_order(b, live);
+  int base = 0;
+  for (int e0 = 0; e0 < G; e0 += 64) {
+    int valid;
+    const int c = count(e0 + lane, valid);
+    const int incl = wave_incl_scan(c, lane);
+    const uint64_t hit = __ballot(c > 0 && base + incl - c <= t && t < base + incl);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      r.expert = __builtin_amdgcn_readfirstlane(e0 + l);
+      r.valid = __builtin_amdgcn_readfirstlane(__shfl(valid, l, 64));
+      r.local = __builtin_amdgcn_readfirstlane(t - base - __shfl(incl - c, l, 64));
+      return r;
+    }
+    base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+  }
+  return r;
 }
 
 struct PipeArgs {
@@ -553,29 +642,29 @@ __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
     pipe_split_tile<Cfg>(args, v, tt, part, part * KB / args.parts, (part + 1) * KB / args.parts);
     return;
   }
-  const int t = xcd_tile_order(blockIdx.x, KIND == kDense ? args.full_tiles : gridDim.x);
   const int NB = (int)((p.N + kKBlock - 1) / kKBlock);
   const int KB = (int)(p.K / kKBlock);
   TileView v;
   int tm, tn;
   if (KIND == kMasked) {
-    const int per_expert = p.tiles_m * p.tiles_n;
-    const int e = t / per_expert;
-    grouped_tile<Cfg::GROUP_M>(t - e * per_expert, p.tiles_m, p.tiles_n, tm, tn);
-    int valid = p.masked_m[e];
-    valid = valid < 0 ? 0 : (valid > (int)p.M ? (int)p.M : valid);
+    // only the live tiles are dealt out: the grid covers every expert at full
+    // height, the workgroups past the live count leave at once
+    const MaskedTile mt = masked_tile<Cfg::BM>(p.masked_m, p.G, (int)p.M, p.tiles_n, blockIdx.x);
+    if (mt.expert < 0) return;
+    const int e = mt.expert, valid = mt.valid;
+    grouped_tile<Cfg::GROUP_M>(mt.local, (valid + Cfg::BM - 1) / Cfg::BM, p.tiles_n, tm, tn);
     v.m0 = (int64_t)tm * Cfg::BM;
     v.n0 = (int64_t)tn * Cfg::BN;
-    if (v.m0 >= valid) return;  // whole tile past the expert's valid rows
     v.A = p.A + (int64_t)e * p.M * p.K;
     v.sfA = p.sfA + (int64_t)e * p.M * KB;
     v.C = p.C + (int64_t)e * p.M * p.N;
     v.B = p.B + (int64_t)e * p.N * p.K;
     v.sfB = p.sfB + (int64_t)e * NB * KB;
-    v.rows = p.M;
+    v.rows = valid;  // rows past masked_m are never read
     pipe_tile<Cfg, KIND>(p, v, e, valid);
     return;
   }
+  const int t = xcd_tile_order(blockIdx.x, KIND == kDense ? args.full_tiles : gridDim.x);
   grouped_tile<Cfg::GROUP_M>(t, p.tiles_m, p.tiles_n, tm, tn);
   v.m0 = (int64_t)tm * Cfg::BM;
   v.n0 = (int64_t)tn * Cfg::BN;
@@ -590,26 +679,32 @@ __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
     return;
   }
   // contiguous: one pass per distinct expert id among the tile's rows, in
-  // increasing id order (one pass when segments are BM-aligned)
+  // increasing id order (one pass when segments are BM-aligned). s_half[h] records
+  // that 64-row half h holds a row of the current expert; a wave whose half holds
+  // none (padding, or another expert's rows) only moves operands.
   __shared__ int s_next;
+  __shared__ int s_half[Cfg::BM / 64];
+  if (threadIdx.x < Cfg::BM / 64) s_half[threadIdx.x] = -1;
+  int id = -1;
+  if (threadIdx.x < Cfg::BM) {
+    const int64_t row = v.m0 + threadIdx.x;
+    if (row < p.M) id = p.m_indices[row];
+  }
   int prev = -1;
   for (;;) {
     if (threadIdx.x == 0) s_next = 0x7FFFFFFF;
     __syncthreads();
-    if (threadIdx.x < Cfg::BM) {
-      const int64_t row = v.m0 + threadIdx.x;
-      if (row < p.M) {
-        const int id = p.m_indices[row];
-        if (id > prev && id < p.G) atomicMin(&s_next, id);
-      }
-    }
+    if (id > prev && id < p.G) atomicMin(&s_next, id);
     __syncthreads();
-    const int e = s_next;
+    const int e = __builtin_amdgcn_readfirstlane(s_next);
+    if (id == e) s_half[threadIdx.x >> 6] = e;
     __syncthreads();
     if (e == 0x7FFFFFFF) break;
+    const int wm = (int)(threadIdx.x >> 6) / Cfg::WAVES_N;
+    const bool any_row = __builtin_amdgcn_readfirstlane(s_half[wm]) == e;
     v.B = p.B + (int64_t)e * p.N * p.K;
     v.sfB = p.sfB + (int64_t)e * NB * KB;
-    pipe_tile<Cfg, KIND>(p, v, e, (int)p.M);
+    pipe_tile<Cfg, KIND>(p, v, e, (int)p.M, any_row);
     prev = e;
   }
 }

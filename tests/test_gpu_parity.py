@@ -315,6 +315,30 @@ def test_masked_integer_exact_bitwise():
         assert_bitwise(g[produced], r[produced], "masked int")
 
 
+def test_masked_many_experts_bitwise():
+    # more than 64 experts: the device-side tile schedule scans the counts in
+    # several 64-wide chunks; empty experts sit at chunk edges
+    rng = np.random.default_rng(41)
+    G, M_max, N, K = 70, 130, 272, 256
+    A, B, sfA, sfB = int_operands(rng, G * M_max, N, K, G=G)
+    A, sfA = A.reshape(G, M_max, K), sfA.reshape(G, M_max, K // 128)
+    masked_m = rng.integers(0, M_max + 1, size=G).astype(np.int32)
+    masked_m[[0, 63, 64, 69]] = [0, 0, 130, 0]
+    g, init = run_masked(A, B, sfA, sfB, masked_m)
+    r, produced = oracle.grouped_masked(A, B, sfA, sfB, masked_m)
+    assert np.array_equal(g[~produced], init[~produced])
+    assert_bitwise(g[produced], r[produced], "masked G=70")
+
+
+def test_masked_all_empty_untouched():
+    rng = np.random.default_rng(43)
+    G, M_max, N, K = 5, 64, 144, 256
+    A, B, sfA, sfB = int_operands(rng, G * M_max, N, K, G=G)
+    A, sfA = A.reshape(G, M_max, K), sfA.reshape(G, M_max, K // 128)
+    g, init = run_masked(A, B, sfA, sfB, np.array([0, -3, 0, 0, 0], dtype=np.int32))
+    assert np.array_equal(g, init), "an all-empty call wrote output"
+
+
 def test_masked_workload_sampled():
     w = synth.workload("moe_mask", pad_code=synth.FP8_NAN_CODE)
     G, M_max, N, K = w.shape
