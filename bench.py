@@ -49,6 +49,7 @@ WORKLOADS = {
     "moe_cont": ["moe_cont"],
     "moe_mask": ["moe_mask"],
     "small": ["small"],
+    "quant": ["quant_act"],
 }
 DESCRIPTIONS = {
     "decode": "dense NT decode, M=64: 64x2112x7168 + 64x32768x512",
@@ -56,7 +57,10 @@ DESCRIPTIONS = {
     "moe_cont": "MoE grouped contiguous, 32 experts, N=4096, K=7168, 8192 Zipf-routed tokens",
     "moe_mask": "MoE grouped masked, 32 experts x 256 rows, N=7168, K=2048",
     "small": "dense NT 128x256x512",
+    "quant": "per-token 1x128 FP8 quantization of bf16 activations [4096][18432] "
+             "(the prefill GEMM's A operand and sfA)",
 }
+QUANT_SHAPES = {"quant_act": (4096, 18432, 3001)}  # M, K, seed of the N(0,1) rows
 
 
 def kernel_source_hash() -> str:
@@ -130,6 +134,65 @@ class Gemm:
         else:
             dg.m_grouped_fp8_gemm_nt_masked(s["A"], s["B"], s["C"], s["sfA"], s["sfB"], s["idx"],
                                             int(self.w.masked_m.mean()))
+
+
+class Quant:
+    """The per-token 1x128 activation quantizer over bf16 activations [M][K]: one read
+    of x (2 bytes a value), one write of the codes (1 byte) and of the scales (4 bytes
+    per 128 values)."""
+
+    def __init__(self, name, M, K, seed):
+        import torch
+        import synth
+        self.name, self.kind = name, "quant"
+        # input preparation: seeded N(0,1) values rounded to bf16
+        self.x_host = torch.from_numpy(synth.normal_rows(seed, M, K)).to(torch.bfloat16)
+        self.flops = 0.0
+        self.bytes = M * K * 2 + M * K + M * (K // 128) * 4
+        self.shape = dict(M=M, K=K, x_dtype="bf16")
+        self.footprint = self.bytes
+
+    def upload(self, copies: int):
+        import torch
+        dev = torch.device("cuda:0")
+        M, K = self.shape["M"], self.shape["K"]
+        x = self.x_host.to(dev)
+        self.sets = [dict(x=x if i == 0 else x.clone(),
+                          codes=torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev),
+                          sf=torch.empty((M, K // 128), dtype=torch.float32, device=dev))
+                     for i in range(copies)]
+
+    def launch(self, i: int):
+        import fp8_block_scaled_dg_amd as dg
+        s = self.sets[i % len(self.sets)]
+        dg.quantize_fp8_1x128(s["x"], s["codes"], s["sf"])
+
+
+def quant_oracle_leg(q, last_set: int, budget_values: float = 8e6):
+    """The oracle's block quantizer on a seeded sample of whole rows, timed and scaled
+    to the whole tensor; the last timed step's codes and scales at those rows must
+    equal it byte for byte."""
+    import numpy as np
+    import torch
+    import oracle
+    M, K = q.shape["M"], q.shape["K"]
+    take = int(min(M, max(1, budget_values // K)))
+    rows = np.sort(np.random.default_rng(12345).choice(M, take, replace=False))
+    x = q.x_host[torch.from_numpy(rows)].to(torch.float32).numpy()
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < 1.0:
+        t0 = time.perf_counter()
+        rc, rs = oracle.quantize_blocks(x, 1, 128)
+        dt += time.perf_counter() - t0
+        reps += 1
+    dt /= reps
+    s = q.sets[last_set % len(q.sets)]
+    codes = s["codes"].view(torch.uint8).cpu().numpy()[rows]
+    sf = s["sf"].cpu().numpy()[rows]
+    check = dict(n=int(rc.size), code_mismatch=int((codes != rc).sum()),
+                 scale_mismatch=int((sf.view(np.uint32) != rs.view(np.uint32)).sum()))
+    sample = f"{q.name}: {take} of {M} rows x {K} values, {dt:.3f} s (mean of {reps})"
+    return dt * M / take, sample, {q.name: check}
 
 
 def oracle_leg(gemms, last_set: int, budget_macs: float = 4e9):
@@ -228,7 +291,8 @@ def main():
         if args.gemm not in names:
             sys.exit(f"--gemm {args.gemm} is not part of workload {args.workload}: {names}")
         names = [args.gemm]
-    gemms = [Gemm(n, synth.workload(n)) for n in names]
+    gemms = [Quant(n, *QUANT_SHAPES[n]) if n in QUANT_SHAPES else Gemm(n, synth.workload(n))
+             for n in names]
     step_footprint = sum(g.footprint for g in gemms)
     copies = max(1, -(-ROTATE_BYTES // step_footprint))
     for g in gemms:
@@ -278,7 +342,7 @@ def main():
                          alg_bytes=g.bytes, alg_flops=g.flops))
     step_bytes = sum(g.bytes for g in gemms)
     step_flops = sum(g.flops for g in gemms)
-    memory_bound = args.workload in ("decode",)
+    memory_bound = args.workload in ("decode", "quant")
     if memory_bound:
         value, unit = step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
     else:
@@ -303,7 +367,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        per_step, sample, checks = oracle_leg(gemms, args.warmup + K - 1)
+        if args.workload == "quant":
+            per_step, sample, checks = quant_oracle_leg(gemms[0], args.warmup + K - 1)
+        else:
+            per_step, sample, checks = oracle_leg(gemms, args.warmup + K - 1)
         import oracle
         cores = oracle.num_threads()
         cpu_value = (step_bytes / per_step / 1e9) if memory_bound else (step_flops / per_step / 1e12)
@@ -322,12 +389,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8",
+        "dtype": "fp32" if args.workload == "quant" else "fp8",
         "data": "synthetic",
-        "config": {"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) quantized to "
-                   "e4m3fn, A per 1x128, B per 128x128, power-of-two scales",
-                   "accumulate": "fp32", "output": "bf16", "parallelism": "single GPU",
-                   "rotation_copies": copies},
+        "config": ({"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) rounded "
+                    "to bf16", "output": "e4m3fn codes + fp32 power-of-two scale per 1x128",
+                    "parallelism": "single GPU", "rotation_copies": copies}
+                   if args.workload == "quant" else
+                   {"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) quantized to "
+                    "e4m3fn, A per 1x128, B per 128x128, power-of-two scales",
+                    "accumulate": "fp32", "output": "bf16", "parallelism": "single GPU",
+                    "rotation_copies": copies}),
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kern,

@@ -11,6 +11,7 @@ article, deepseek.csdn.net, section 4.2 "advanced tuning"):
 * ``fp8_gemm_nt(a, b, c, a_sf, b_sf)``
 * ``m_grouped_fp8_gemm_nt_contiguous(a, b, c, a_sf, b_sf, m_indices)``
 * ``m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None)``
+* ``quantize_fp8_1x128(x, codes=None, sf=None)``: activations -> (A codes, sfA)
 
 Operands: ``a``/``b`` are ``torch.float8_e4m3fn`` (``torch.uint8`` holding e4m3fn
 codes is accepted too), ``a_sf``/``b_sf`` ``torch.float32``, ``c`` ``torch.bfloat16``
@@ -50,12 +51,16 @@ lib.dg_last_error_detail.argtypes = []
 lib.dg_describe_config.restype = ctypes.c_int
 lib.dg_describe_config.argtypes = [_i32, _i64, _i64, _i64, _i32, _i64, ctypes.c_char_p, _i64]
 
+lib.dg_quantize_fp8_1x128.restype = ctypes.c_int
+lib.dg_quantize_fp8_1x128.argtypes = [_vp, _i32, _vp, _vp, _i64, _i64, _vp]
+
 lib.dg_num_configs.restype = _i32
 lib.dg_num_configs.argtypes = []
 lib.dg_config_name.restype = ctypes.c_char_p
 lib.dg_config_name.argtypes = [_i32]
 
 KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED = 0, 1, 2
+DTYPE_F32, DTYPE_BF16 = 0, 1
 BLOCK = 128
 
 
@@ -160,6 +165,34 @@ def m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None)
             masked_m.data_ptr(), G, M_max, N, K, em, _stream(dev)))
 
 
+def quantize_fp8_1x128(x, codes=None, sf=None):
+    """Per-token 1x128 quantization of x [M, K] (float32 or bfloat16): returns
+    (codes [M, K] torch.float8_e4m3fn, sf [M, K/128] torch.float32), written into the
+    given tensors when passed (new tensors otherwise)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    if x.dtype == torch.float32:
+        dtype = DTYPE_F32
+    elif x.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    else:
+        raise TypeError(f"x must be torch.float32 or torch.bfloat16, got {x.dtype}")
+    M, K = x.shape
+    dev = x.device
+    _dev(x, "x", dev)
+    if codes is None:
+        codes = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    if sf is None:
+        sf = torch.empty((M, K // BLOCK), dtype=torch.float32, device=dev)
+    _fp8(codes, "codes")
+    _need(codes, "codes", codes.dtype, (M, K), dev)
+    _need(sf, "sf", torch.float32, (M, K // BLOCK), dev)
+    with torch.cuda.device(dev):
+        check(lib.dg_quantize_fp8_1x128(x.data_ptr(), dtype, codes.data_ptr(), sf.data_ptr(),
+                                        M, K, _stream(dev)))
+    return codes, sf
+
+
 def describe_config(kind: int, M: int, N: int, K: int, G: int = 1, expected_m: int = 0) -> str:
     buf = ctypes.create_string_buffer(128)
     check(lib.dg_describe_config(kind, M, N, K, G, expected_m, buf, 128))
@@ -171,4 +204,4 @@ def config_names() -> list[str]:
 
 
 __all__ = ["config_names", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
-           "describe_config", "DGError", "lib", "LIB_PATH"]
+           "quantize_fp8_1x128", "describe_config", "DGError", "lib", "LIB_PATH"]

@@ -22,6 +22,7 @@
 #include "../../include/dg.h"
 #include "gemm_kernel.hpp"
 #include "pipe_kernel.hpp"
+#include "quant_kernel.hpp"
 #include "skinny_kernel.hpp"
 #include "stream_kernel.hpp"
 
@@ -520,6 +521,35 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
   const int id = select_config(kMasked, em, M_max, N, K, G);
   maybe_print(kMasked, M_max, N, K, G, id);
   return launch(kMasked, id, p, G, (hipStream_t)stream);
+}
+
+dg_status dg_quantize_fp8_1x128(const void* x, int32_t x_dtype, void* codes, float* sf,
+                                int64_t M, int64_t K, void* stream) {
+  g_detail[0] = 0;
+  if (x_dtype != DG_DTYPE_F32 && x_dtype != DG_DTYPE_BF16)
+    return fail(DG_ERR_BAD_SHAPE, "x_dtype=%d is neither DG_DTYPE_F32 nor DG_DTYPE_BF16", x_dtype);
+  if (M < 0 || K < 0)
+    return fail(DG_ERR_BAD_SHAPE, "negative size (M=%lld, K=%lld)", (long long)M, (long long)K);
+  if (K % kKBlock != 0) return fail(DG_ERR_BAD_SHAPE, "K=%lld is not a multiple of 128", (long long)K);
+  if (M == 0 || K == 0) return DG_OK;
+  if (!x || !codes || !sf) return fail(DG_ERR_NULL_POINTER, "NULL x, codes or sf");
+  if (!aligned(x, 16) || !aligned(codes, 16))
+    return fail(DG_ERR_MISALIGNED, "x and codes must be 16-byte aligned");
+  if (!aligned(sf, 4)) return fail(DG_ERR_MISALIGNED, "sf must be 4-byte aligned");
+  if (M > ((int64_t)1 << 40) / K) return fail(DG_ERR_UNSUPPORTED_SHAPE, "M*K beyond 2^40");
+  const int64_t nblocks = M * (K / kKBlock);
+  const int64_t per_wg = (int64_t)(kQuantThreads / 64) * kQuantBlocksPerWave * kQuantUnroll;
+  int64_t grid = (nblocks + per_wg - 1) / per_wg;
+  if (grid > 8 * kCUs) grid = 8 * kCUs;  // grid-stride beyond eight workgroups per CU
+  if (x_dtype == DG_DTYPE_BF16)
+    hipLaunchKernelGGL(quant_kernel<true>, dim3((unsigned)grid), dim3(kQuantThreads), 0,
+                       (hipStream_t)stream, x, (uint8_t*)codes, sf, nblocks);
+  else
+    hipLaunchKernelGGL(quant_kernel<false>, dim3((unsigned)grid), dim3(kQuantThreads), 0,
+                       (hipStream_t)stream, x, (uint8_t*)codes, sf, nblocks);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "quant_kernel: %s", hipGetErrorString(err));
+  return DG_OK;
 }
 
 int32_t dg_num_configs(void) { return kNumCfg; }

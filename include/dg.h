@@ -53,7 +53,8 @@ extern "C" {
 typedef enum dg_status {
   DG_OK = 0,
   DG_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                    */
-  DG_ERR_BAD_SHAPE = 2,         /* negative size, K % 128 != 0, N % 16 != 0, G<1 */
+  DG_ERR_BAD_SHAPE = 2,         /* negative size, K % 128 != 0, N % 16 != 0, G<1, */
+                                /* or an unknown dg_dtype                         */
   DG_ERR_UNSUPPORTED_SHAPE = 3, /* valid but beyond what the kernels index       */
   DG_ERR_MISALIGNED = 4,        /* A/B/C not 16-byte or scales not 4-byte aligned */
   DG_ERR_NO_DEVICE = 5,         /* no usable gfx950 device                       */
@@ -107,6 +108,27 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
                                           const int32_t* masked_m, int32_t G,
                                           int64_t M_max, int64_t N, int64_t K,
                                           int64_t expected_m, void* hip_stream);
+
+/*
+ * Per-token 1x128 activation quantizer: the step that turns activations into the
+ * A operand and sfA of the calls above (one scaling factor per small block, each
+ * block then spanning the FP8 range on its own: launch article, section 1.2).
+ *   x      [M][K] row-major, fp32 (x_dtype = DG_DTYPE_F32) or bf16 (DG_DTYPE_BF16)
+ *   codes  e4m3fn [M][K] (output)       sf  fp32 [M][K/128] (output)
+ * For each block of 128 values (row m, K-block kb): amax = max |x|; e = the least
+ * integer with amax <= 448 * 2^e (e = 0 when amax = 0); sf[m][kb] = 2^e as fp32;
+ * each code is the e4m3fn value nearest to x / 2^e, ties to the even code, a zero
+ * keeping the sign of x. Exact for every finite input (fp32 subnormals included;
+ * 2^e below the fp32 range stores 0, as a float conversion of 2^e would); codes
+ * and scales of a block holding an infinity or NaN are unspecified.
+ * K % 128 == 0; x and codes 16-byte aligned, sf 4-byte aligned; M * K <= 2^40.
+ * M == 0 or K == 0 returns DG_OK and launches nothing. Same stream, ownership and
+ * error conventions as the GEMM calls.
+ */
+typedef enum dg_dtype { DG_DTYPE_F32 = 0, DG_DTYPE_BF16 = 1 } dg_dtype;
+
+dg_status dg_quantize_fp8_1x128(const void* x, int32_t x_dtype, void* codes, float* sf,
+                                int64_t M, int64_t K, void* hip_stream);
 
 /* Static string naming a status. */
 const char* dg_status_string(dg_status s);

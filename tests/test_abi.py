@@ -124,3 +124,29 @@ def test_binding_rejects_cpu_tensors(dg):
         dg.fp8_gemm_nt(a, b, c, torch.ones(64, 1), torch.ones(1, 1))
     with pytest.raises(TypeError):
         dg.fp8_gemm_nt(a.float(), b, c, torch.ones(64, 1), torch.ones(1, 1))
+
+
+def test_quantizer_rejects_bad_arguments(dg):
+    q = dg.lib.dg_quantize_fp8_1x128
+    F32, BF16 = dg.DTYPE_F32, dg.DTYPE_BF16
+    assert status(dg, q(None, F32, FAKE, FAKE, 4, 256, None)) == "DG_ERR_NULL_POINTER"
+    assert status(dg, q(FAKE, BF16, FAKE, None, 4, 256, None)) == "DG_ERR_NULL_POINTER"
+    assert status(dg, q(FAKE, F32, FAKE, FAKE, 4, 200, None)) == "DG_ERR_BAD_SHAPE"
+    assert status(dg, q(FAKE, F32, FAKE, FAKE, -1, 256, None)) == "DG_ERR_BAD_SHAPE"
+    assert status(dg, q(FAKE, 7, FAKE, FAKE, 4, 256, None)) == "DG_ERR_BAD_SHAPE"
+    assert status(dg, q(FAKE + 4, F32, FAKE, FAKE, 4, 256, None)) == "DG_ERR_MISALIGNED"
+    assert status(dg, q(FAKE, F32, FAKE + 8, FAKE, 4, 256, None)) == "DG_ERR_MISALIGNED"
+    assert status(dg, q(FAKE, F32, FAKE, FAKE + 2, 4, 256, None)) == "DG_ERR_MISALIGNED"
+    assert status(dg, q(FAKE, F32, FAKE, FAKE, 1 << 36, 1 << 10, None)) == \
+        "DG_ERR_UNSUPPORTED_SHAPE"
+    # nothing to produce
+    assert status(dg, q(None, F32, None, None, 0, 256, None)) == "DG_OK"
+    assert status(dg, q(None, BF16, None, None, 4, 0, None)) == "DG_OK"
+
+
+def test_quantizer_binding_checks_dtype_and_device(dg):
+    import torch
+    with pytest.raises(TypeError):
+        dg.quantize_fp8_1x128(torch.zeros(2, 128, dtype=torch.float16, device="cpu"))
+    with pytest.raises(ValueError):
+        dg.quantize_fp8_1x128(torch.zeros(2, 128, dtype=torch.float32, device="cpu"))
