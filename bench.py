@@ -75,7 +75,7 @@ def kernel_source_hash() -> str:
 class Gemm:
     """One GEMM of the workload: host inputs, device copies, algorithmic work."""
 
-    def __init__(self, name, w):
+    def __init__(self, name, w, sfa_layout: str = "f32"):
         import numpy as np
         self.name, self.w = name, w
         self.kind = type(w).__name__.lower()
@@ -94,21 +94,24 @@ class Gemm:
             Ga = int((np.clip(w.masked_m, 0, M) > 0).sum())
             meta = 4 * G
         KB, NB = K // 128, (N + 127) // 128
+        sfa_row = 4 * ((KB + 3) // 4) if sfa_layout == "ue8m0" else 4 * KB  # bytes per row
         self.flops = 2.0 * Mv * N * K
-        self.bytes = (Mv * K + Ga * N * K + 4 * Mv * KB + 4 * Ga * NB * KB + 2 * Mv * N + meta)
+        self.bytes = (Mv * K + Ga * N * K + Mv * sfa_row + 4 * Ga * NB * KB + 2 * Mv * N + meta)
         self.shape = dict(M=M, N=N, K=K, G=G, valid_rows=Mv, active_experts=Ga)
         self.footprint = (w.A.nbytes + w.B.nbytes + w.sfA.nbytes + w.sfB.nbytes
                           + (M * N * 2 if self.kind != "masked" else G * M * N * 2))
 
-    def upload(self, copies: int):
+    def upload(self, copies: int, sfa_layout: str = "f32"):
         import torch
+        import synth
         dev = torch.device("cuda:0")
 
         def t(x):
             return torch.from_numpy(x).to(dev)
 
+        sfa = synth.pack_ue8m0(self.w.sfA) if sfa_layout == "ue8m0" else self.w.sfA
         base = dict(A=t(self.w.A).view(torch.float8_e4m3fn), B=t(self.w.B).view(torch.float8_e4m3fn),
-                    sfA=t(self.w.sfA), sfB=t(self.w.sfB))
+                    sfA=t(sfa), sfB=t(self.w.sfB))
         if self.kind == "contiguous":
             base["idx"] = t(self.w.m_indices)
             cshape = (self.w.A.shape[0], self.w.B.shape[1])
@@ -152,7 +155,7 @@ class Quant:
         self.shape = dict(M=M, K=K, x_dtype="bf16")
         self.footprint = self.bytes
 
-    def upload(self, copies: int):
+    def upload(self, copies: int, sfa_layout: str = "f32"):
         import torch
         dev = torch.device("cuda:0")
         M, K = self.shape["M"], self.shape["K"]
@@ -195,7 +198,7 @@ def quant_oracle_leg(q, last_set: int, budget_values: float = 8e6):
     return dt * M / take, sample, {q.name: check}
 
 
-def oracle_leg(gemms, last_set: int, budget_macs: float = 4e9):
+def oracle_leg(gemms, last_set: int, sfa_layout: str = "f32", budget_macs: float = 4e9):
     """CPU baseline: the oracle over the step's produced outputs -- every output when a
     GEMM is at most budget_macs multiply-adds, else a seeded sample of whole rows --
     timed on the host cores and scaled to the whole step; and the comparison of the
@@ -206,9 +209,13 @@ def oracle_leg(gemms, last_set: int, budget_macs: float = 4e9):
     from tests.parity import report
 
     per_step, checks, samples = 0.0, {}, []
+    import synth
     for g in gemms:
         w = g.w
         N, K = g.shape["N"], g.shape["K"]
+        # the oracle reads the scales in the layout the GPU was given
+        sfA = (oracle.unpack_ue8m0(synth.pack_ue8m0(w.sfA), K // 128) if sfa_layout == "ue8m0"
+               else w.sfA)
         if g.kind == "dense":
             rows = np.arange(g.shape["M"])
         elif g.kind == "contiguous":
@@ -227,12 +234,12 @@ def oracle_leg(gemms, last_set: int, budget_macs: float = 4e9):
         while reps == 0 or dt < 1.0:  # repeat short samples for a stable time
             t0 = time.perf_counter()
             if g.kind == "dense":
-                r = oracle.gemm_nt_at(w.A, w.B, w.sfA, w.sfB, ri, ni)
+                r = oracle.gemm_nt_at(w.A, w.B, sfA, w.sfB, ri, ni)
             elif g.kind == "contiguous":
-                r = oracle.grouped_contiguous_at(w.A, w.B, w.sfA, w.sfB, w.m_indices, ri, ni)
+                r = oracle.grouped_contiguous_at(w.A, w.B, sfA, w.sfB, w.m_indices, ri, ni)
             else:
                 M_max = g.shape["M"]
-                r = oracle.grouped_masked_at(w.A, w.B, w.sfA, w.sfB, w.masked_m, ri // M_max,
+                r = oracle.grouped_masked_at(w.A, w.B, sfA, w.sfB, w.masked_m, ri // M_max,
                                              ri % M_max, ni)
             dt += time.perf_counter() - t0
             reps += 1
@@ -258,6 +265,8 @@ def main():
                          "time has passed, so that the GPU clocks have left their idle state")
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sfa", choices=("f32", "ue8m0"), default="f32",
+                    help="layout of the A scales: fp32 values, or packed UE8M0 exponent bytes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (to calibrate HBM counters)")
     ap.add_argument("--gemm", default=None,
@@ -291,12 +300,12 @@ def main():
         if args.gemm not in names:
             sys.exit(f"--gemm {args.gemm} is not part of workload {args.workload}: {names}")
         names = [args.gemm]
-    gemms = [Quant(n, *QUANT_SHAPES[n]) if n in QUANT_SHAPES else Gemm(n, synth.workload(n))
+    gemms = [Quant(n, *QUANT_SHAPES[n]) if n in QUANT_SHAPES else Gemm(n, synth.workload(n), args.sfa)
              for n in names]
     step_footprint = sum(g.footprint for g in gemms)
     copies = max(1, -(-ROTATE_BYTES // step_footprint))
     for g in gemms:
-        g.upload(copies)
+        g.upload(copies, args.sfa)
     torch.cuda.synchronize()
 
     warm = 0
@@ -370,7 +379,7 @@ def main():
         if args.workload == "quant":
             per_step, sample, checks = quant_oracle_leg(gemms[0], args.warmup + K - 1)
         else:
-            per_step, sample, checks = oracle_leg(gemms, args.warmup + K - 1)
+            per_step, sample, checks = oracle_leg(gemms, args.warmup + K - 1, args.sfa)
         import oracle
         cores = oracle.num_threads()
         cpu_value = (step_bytes / per_step / 1e9) if memory_bound else (step_flops / per_step / 1e12)
@@ -397,6 +406,7 @@ def main():
                    if args.workload == "quant" else
                    {"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) quantized to "
                     "e4m3fn, A per 1x128, B per 128x128, power-of-two scales",
+                    "sfa_layout": "packed UE8M0" if args.sfa == "ue8m0" else "fp32",
                     "accumulate": "fp32", "output": "bf16", "parallelism": "single GPU",
                     "rotation_copies": copies}),
         "roofline": roof,

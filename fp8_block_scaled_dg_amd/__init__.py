@@ -15,7 +15,9 @@ article, deepseek.csdn.net, section 4.2 "advanced tuning"):
 
 Operands: ``a``/``b`` are ``torch.float8_e4m3fn`` (``torch.uint8`` holding e4m3fn
 codes is accepted too), ``a_sf``/``b_sf`` ``torch.float32``, ``c`` ``torch.bfloat16``
-and the index tensors ``torch.int32``, all on the same GPU.
+and the index tensors ``torch.int32``, all on the same GPU. An ``a_sf`` of dtype
+``torch.int32`` and last dimension ceil(K/512) is the packed UE8M0 layout (one
+exponent byte per K-block, four per word) and selects the ``*_ue8m0`` calls.
 """
 from __future__ import annotations
 
@@ -51,6 +53,13 @@ lib.dg_last_error_detail.argtypes = []
 lib.dg_describe_config.restype = ctypes.c_int
 lib.dg_describe_config.argtypes = [_i32, _i64, _i64, _i64, _i32, _i64, ctypes.c_char_p, _i64]
 
+lib.dg_fp8_gemm_nt_ue8m0.restype = ctypes.c_int
+lib.dg_fp8_gemm_nt_ue8m0.argtypes = lib.dg_fp8_gemm_nt.argtypes
+lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.restype = ctypes.c_int
+lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.argtypes = \
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
+lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.restype = ctypes.c_int
+lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
 lib.dg_quantize_fp8_1x128.restype = ctypes.c_int
 lib.dg_quantize_fp8_1x128.argtypes = [_vp, _i32, _vp, _vp, _i64, _i64, _vp]
 
@@ -104,8 +113,20 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _a_sf_layout(a_sf, lead: tuple, K: int, dev):
+    """(packed?, expected shape) of a_sf: torch.float32 [..., K/128], or torch.int32
+    [..., ceil(K/512)] holding packed UE8M0 bytes (one per K-block, 4 per word)."""
+    if a_sf.dtype == torch.int32:
+        shape = lead + ((K // BLOCK + 3) // 4,)
+        _need(a_sf, "a_sf", torch.int32, shape, dev)
+        return True
+    _need(a_sf, "a_sf", torch.float32, lead + (K // BLOCK,), dev)
+    return False
+
+
 def fp8_gemm_nt(a, b, c, a_sf, b_sf) -> None:
-    """c[M][N] (bf16) = block-scaled a[M][K] x b[N][K]^T; writes c in place."""
+    """c[M][N] (bf16) = block-scaled a[M][K] x b[N][K]^T; writes c in place. a_sf is
+    fp32 [M, K/128], or int32 [M, ceil(K/512)] in the packed UE8M0 layout."""
     _fp8(a, "a"), _fp8(b, "b")
     if a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D")
@@ -115,11 +136,12 @@ def fp8_gemm_nt(a, b, c, a_sf, b_sf) -> None:
     _dev(a, "a", dev)
     _need(b, "b", b.dtype, (N, K), dev)
     _need(c, "c", torch.bfloat16, (M, N), dev)
-    _need(a_sf, "a_sf", torch.float32, (M, K // BLOCK), dev)
+    packed = _a_sf_layout(a_sf, (M,), K, dev)
     _need(b_sf, "b_sf", torch.float32, ((N + BLOCK - 1) // BLOCK, K // BLOCK), dev)
+    fn = lib.dg_fp8_gemm_nt_ue8m0 if packed else lib.dg_fp8_gemm_nt
     with torch.cuda.device(dev):
-        check(lib.dg_fp8_gemm_nt(a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(),
-                                 b_sf.data_ptr(), M, N, K, _stream(dev)))
+        check(fn(a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
+                 M, N, K, _stream(dev)))
 
 
 def m_grouped_fp8_gemm_nt_contiguous(a, b, c, a_sf, b_sf, m_indices) -> None:
@@ -134,11 +156,13 @@ def m_grouped_fp8_gemm_nt_contiguous(a, b, c, a_sf, b_sf, m_indices) -> None:
     _dev(a, "a", dev)
     _need(b, "b", b.dtype, (G, N, K), dev)
     _need(c, "c", torch.bfloat16, (M, N), dev)
-    _need(a_sf, "a_sf", torch.float32, (M, K // BLOCK), dev)
+    packed = _a_sf_layout(a_sf, (M,), K, dev)
     _need(b_sf, "b_sf", torch.float32, (G, (N + BLOCK - 1) // BLOCK, K // BLOCK), dev)
     _need(m_indices, "m_indices", torch.int32, (M,), dev)
+    fn = (lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 if packed
+          else lib.dg_m_grouped_fp8_gemm_nt_contiguous)
     with torch.cuda.device(dev):
-        check(lib.dg_m_grouped_fp8_gemm_nt_contiguous(
+        check(fn(
             a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
             m_indices.data_ptr(), M, N, K, G, _stream(dev)))
 
@@ -155,12 +179,13 @@ def m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None)
     _dev(a, "a", dev)
     _need(b, "b", b.dtype, (G, N, K), dev)
     _need(c, "c", torch.bfloat16, (G, M_max, N), dev)
-    _need(a_sf, "a_sf", torch.float32, (G, M_max, K // BLOCK), dev)
+    packed = _a_sf_layout(a_sf, (G, M_max), K, dev)
     _need(b_sf, "b_sf", torch.float32, (G, (N + BLOCK - 1) // BLOCK, K // BLOCK), dev)
     _need(masked_m, "masked_m", torch.int32, (G,), dev)
     em = int(expected_m) if expected_m is not None else 0
+    fn = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0 if packed else lib.dg_m_grouped_fp8_gemm_nt_masked
     with torch.cuda.device(dev):
-        check(lib.dg_m_grouped_fp8_gemm_nt_masked(
+        check(fn(
             a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
             masked_m.data_ptr(), G, M_max, N, K, em, _stream(dev)))
 

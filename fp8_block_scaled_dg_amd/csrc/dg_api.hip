@@ -181,8 +181,11 @@ dg_status launch_skinny(const Problem& p0, int64_t blocks, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute((const void*)skinny_kernel<Cfg>,
+    attr_err = hipFuncSetAttribute((const void*)skinny_kernel<Cfg, false>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
+    if (attr_err == hipSuccess)
+      attr_err = hipFuncSetAttribute((const void*)skinny_kernel<Cfg, true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
   });
   if (attr_err != hipSuccess)
     return fail(DG_ERR_LAUNCH, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
@@ -210,8 +213,12 @@ dg_status launch_skinny(const Problem& p0, int64_t blocks, hipStream_t stream) {
     dg_status st = get_workspace(stream, part, (size_t)tiles, &a.ws, &a.counters);
     if (st != DG_OK) return st;
   }
-  hipLaunchKernelGGL((skinny_kernel<Cfg>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS_BYTES,
-                     stream, a);
+  if (p0.sfa_packed)
+    hipLaunchKernelGGL((skinny_kernel<Cfg, true>), dim3((unsigned)grid), dim3(Cfg::NT),
+                       Cfg::LDS_BYTES, stream, a);
+  else
+    hipLaunchKernelGGL((skinny_kernel<Cfg, false>), dim3((unsigned)grid), dim3(Cfg::NT),
+                       Cfg::LDS_BYTES, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
   return DG_OK;
@@ -263,7 +270,10 @@ dg_status launch_stream(const Problem& p0, int64_t blocks, hipStream_t stream) {
     dg_status st = get_workspace(stream, part, (size_t)pl.tiles, &a.ws, &a.counters);
     if (st != DG_OK) return st;
   }
-  hipLaunchKernelGGL((stream_kernel<Cfg>), dim3((unsigned)pl.grid), dim3(Cfg::NT), 0, stream, a);
+  if (p0.sfa_packed)
+    hipLaunchKernelGGL((stream_kernel<Cfg, true>), dim3((unsigned)pl.grid), dim3(Cfg::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((stream_kernel<Cfg, false>), dim3((unsigned)pl.grid), dim3(Cfg::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
   return DG_OK;
@@ -402,7 +412,7 @@ dg_status launch(int kind, int id, const Problem& p, int64_t blocks, hipStream_t
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-dg_status check_common(const void* A, const void* B, const void* C, const float* sfA,
+dg_status check_common(const void* A, const void* B, const void* C, const void* sfA,
                        const float* sfB, int64_t N, int64_t K, bool any_output) {
   if (N < 0 || K < 0) return fail(DG_ERR_BAD_SHAPE, "negative size (N=%lld, K=%lld)",
                                   (long long)N, (long long)K);
@@ -442,8 +452,14 @@ const char* dg_status_string(dg_status s) {
 
 const char* dg_last_error_detail(void) { return g_detail; }
 
-dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA,
-                         const float* sfB, int64_t M, int64_t N, int64_t K, void* stream) {
+}  // extern "C"
+
+namespace dg {
+namespace {
+
+// The three GEMM forms with sfA as raw bytes: fp32 values, or packed UE8M0 words.
+dg_status gemm_dense(const void* A, const void* B, void* C, const void* sfA, int packed,
+                     const float* sfB, int64_t M, int64_t N, int64_t K, void* stream) {
   g_detail[0] = 0;
   if (M < 0) return fail(DG_ERR_BAD_SHAPE, "negative M=%lld", (long long)M);
   dg_status s = check_common(A, B, C, sfA, sfB, N, K, M > 0 && N > 0);
@@ -453,7 +469,8 @@ dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA
   p.A = (const uint8_t*)A;
   p.B = (const uint8_t*)B;
   p.C = (uint16_t*)C;
-  p.sfA = sfA;
+  p.sfA = (const uint8_t*)sfA;
+  p.sfa_packed = packed;
   p.sfB = sfB;
   p.M = M;
   p.N = N;
@@ -464,10 +481,9 @@ dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA
   return launch(kDense, id, p, 1, (hipStream_t)stream);
 }
 
-dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const void* B, void* C,
-                                              const float* sfA, const float* sfB,
-                                              const int32_t* m_indices, int64_t M_total,
-                                              int64_t N, int64_t K, int32_t G, void* stream) {
+dg_status gemm_contiguous(const void* A, const void* B, void* C, const void* sfA, int packed,
+                          const float* sfB, const int32_t* m_indices, int64_t M_total,
+                          int64_t N, int64_t K, int32_t G, void* stream) {
   g_detail[0] = 0;
   if (M_total < 0) return fail(DG_ERR_BAD_SHAPE, "negative M_total=%lld", (long long)M_total);
   if (G < 1) return fail(DG_ERR_BAD_SHAPE, "G=%d, need at least one expert", G);
@@ -480,7 +496,8 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const void* B, void
   p.A = (const uint8_t*)A;
   p.B = (const uint8_t*)B;
   p.C = (uint16_t*)C;
-  p.sfA = sfA;
+  p.sfA = (const uint8_t*)sfA;
+  p.sfa_packed = packed;
   p.sfB = sfB;
   p.m_indices = m_indices;
   p.M = M_total;
@@ -492,11 +509,9 @@ dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const void* B, void
   return launch(kContiguous, id, p, 1, (hipStream_t)stream);
 }
 
-dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
-                                          const float* sfA, const float* sfB,
-                                          const int32_t* masked_m, int32_t G, int64_t M_max,
-                                          int64_t N, int64_t K, int64_t expected_m,
-                                          void* stream) {
+dg_status gemm_masked(const void* A, const void* B, void* C, const void* sfA, int packed,
+                      const float* sfB, const int32_t* masked_m, int32_t G, int64_t M_max,
+                      int64_t N, int64_t K, int64_t expected_m, void* stream) {
   g_detail[0] = 0;
   if (M_max < 0) return fail(DG_ERR_BAD_SHAPE, "negative M_max=%lld", (long long)M_max);
   if (G < 1) return fail(DG_ERR_BAD_SHAPE, "G=%d, need at least one expert", G);
@@ -510,7 +525,8 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
   p.A = (const uint8_t*)A;
   p.B = (const uint8_t*)B;
   p.C = (uint16_t*)C;
-  p.sfA = sfA;
+  p.sfA = (const uint8_t*)sfA;
+  p.sfa_packed = packed;
   p.sfB = sfB;
   p.masked_m = masked_m;
   p.M = M_max;
@@ -521,6 +537,53 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
   const int id = select_config(kMasked, em, M_max, N, K, G);
   maybe_print(kMasked, M_max, N, K, G, id);
   return launch(kMasked, id, p, G, (hipStream_t)stream);
+}
+
+}  // namespace
+}  // namespace dg
+
+extern "C" {
+
+dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA,
+                         const float* sfB, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_dense(A, B, C, sfA, 0, sfB, M, N, K, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous(const void* A, const void* B, void* C,
+                                              const float* sfA, const float* sfB,
+                                              const int32_t* m_indices, int64_t M_total,
+                                              int64_t N, int64_t K, int32_t G, void* stream) {
+  return gemm_contiguous(A, B, C, sfA, 0, sfB, m_indices, M_total, N, K, G, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
+                                          const float* sfA, const float* sfB,
+                                          const int32_t* masked_m, int32_t G, int64_t M_max,
+                                          int64_t N, int64_t K, int64_t expected_m,
+                                          void* stream) {
+  return gemm_masked(A, B, C, sfA, 0, sfB, masked_m, G, M_max, N, K, expected_m, stream);
+}
+
+dg_status dg_fp8_gemm_nt_ue8m0(const void* A, const void* B, void* C, const uint32_t* sfA,
+                               const float* sfB, int64_t M, int64_t N, int64_t K,
+                               void* stream) {
+  return gemm_dense(A, B, C, sfA, 1, sfB, M, N, K, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* A, const void* B, void* C,
+                                                    const uint32_t* sfA, const float* sfB,
+                                                    const int32_t* m_indices, int64_t M_total,
+                                                    int64_t N, int64_t K, int32_t G,
+                                                    void* stream) {
+  return gemm_contiguous(A, B, C, sfA, 1, sfB, m_indices, M_total, N, K, G, stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* A, const void* B, void* C,
+                                                const uint32_t* sfA, const float* sfB,
+                                                const int32_t* masked_m, int32_t G,
+                                                int64_t M_max, int64_t N, int64_t K,
+                                                int64_t expected_m, void* stream) {
+  return gemm_masked(A, B, C, sfA, 1, sfB, masked_m, G, M_max, N, K, expected_m, stream);
 }
 
 dg_status dg_quantize_fp8_1x128(const void* x, int32_t x_dtype, void* codes, float* sf,

@@ -44,7 +44,8 @@ struct Problem {
   const uint8_t* A;
   const uint8_t* B;
   uint16_t* C;
-  const float* sfA;
+  const uint8_t* sfA;        // rows of KB fp32 values, or (sfa_packed) of ceil(KB/4)
+                             // little-endian words of UE8M0 bytes, byte kb = K-block kb
   const float* sfB;
   const int32_t* m_indices;  // contiguous only
   const int32_t* masked_m;   // masked only
@@ -54,7 +55,22 @@ struct Problem {
   int32_t G;
   int32_t tiles_m;
   int32_t tiles_n;
+  int32_t sfa_packed;        // 1: sfA in the packed UE8M0 layout
 };
+
+// Bytes of one sfA row: KB fp32 values, or ceil(KB/4) words of UE8M0 bytes.
+__host__ __device__ inline int64_t sfa_row_bytes(int64_t KB, int packed) {
+  return packed ? (KB + 3) / 4 * 4 : KB * 4;
+}
+
+// The scale a UE8M0 byte encodes: 2^(b - 127) (b = 255, NaN in the OCP MX format,
+// is not a valid scale).
+__device__ __forceinline__ float ue8m0_value(uint32_t b) { return ldexpf(1.f, (int)b - 127); }
+
+// sfA of K-block kb from a row's bytes.
+__device__ __forceinline__ float sfa_at(const uint8_t* row, int kb, int packed) {
+  return packed ? ue8m0_value(row[kb]) : ((const float*)row)[kb];
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -88,7 +104,7 @@ struct TileCfg {
 struct TileView {
   const uint8_t* A;    // [rows][K]
   const uint8_t* B;    // [N][K]
-  const float* sfA;    // [rows][KB]
+  const uint8_t* sfA;  // [rows] sfA rows (Problem::sfA layout)
   const float* sfB;    // [NB][KB]
   uint16_t* C;         // [rows][N]
   int64_t rows;        // rows addressable in A / sfA / C
@@ -130,11 +146,12 @@ __device__ __forceinline__ void run_tile(const Problem& p, const TileView& v, in
     b_src[i] = v.B + row * K + c * 16;
     b_dst[i] = r * kKBlock + ((c ^ swz(r)) << 4);
   }
-  const float* sa_src = nullptr;
+  const uint8_t* sa_src = nullptr;
+  const int packed = p.sfa_packed;
   if (tid < BM) {
     int64_t row = v.m0 + tid;
     if (row >= v.rows) row = v.rows - 1;
-    sa_src = v.sfA + row * KB;
+    sa_src = v.sfA + row * sfa_row_bytes(KB, packed);
   }
   const float* sb_src = nullptr;
   if (tid < NBT) {
@@ -152,7 +169,7 @@ __device__ __forceinline__ void run_tile(const Problem& p, const TileView& v, in
     for (int i = 0; i < Cfg::A_CHUNKS; ++i) ra[i] = *(const uint4*)(a_src[i] + koff);
 #pragma unroll
     for (int i = 0; i < Cfg::B_CHUNKS; ++i) rb[i] = *(const uint4*)(b_src[i] + koff);
-    if (tid < BM) rsa = sa_src[kb];
+    if (tid < BM) rsa = sfa_at(sa_src, kb, packed);
     if (tid < NBT) rsb = sb_src[kb];
   };
   auto lstore = [&](int buf) {
@@ -263,7 +280,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(Problem p) {
     v.n0 = (int64_t)tn * Cfg::BN;
     if (v.m0 >= valid) return;  // whole tile past the expert's valid rows
     v.A = p.A + (int64_t)e * p.M * p.K;
-    v.sfA = p.sfA + (int64_t)e * p.M * KB;
+    v.sfA = p.sfA + (int64_t)e * p.M * sfa_row_bytes(KB, p.sfa_packed);
     v.C = p.C + (int64_t)e * p.M * p.N;
     v.B = p.B + (int64_t)e * p.N * p.K;
     v.sfB = p.sfB + (int64_t)e * NB * KB;

@@ -123,6 +123,8 @@ struct PipeThread {
   uint32_t b_off[Cfg::B_DMA];
   uint32_t sa_off;  // this lane's sfA row
   uint32_t sb_off;  // this lane's sfB row
+  int sa_shift;     // sfA's scalar offset for K-block kb is (kb >> sa_shift) * 4 bytes:
+                    // 0 for fp32 values, 2 for packed UE8M0 words (nonzero = packed)
 };
 
 // Raw buffer over [p, p + bytes), bytes < 2^31.
@@ -143,7 +145,7 @@ __device__ __forceinline__ void pipe_issue(const PipeThread<Cfg>& th, int kb, in
   if (SCALES) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sa_rsrc,
                                              DG_LDS(pipe_scale + wave * kScaleWaveBytes), 12,
-                                             th.sa_off, kb * 4, 0, 0);
+                                             th.sa_off, (kb >> th.sa_shift) << 2, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sb_rsrc, DG_LDS(pipe_sfb), 12, th.sb_off, kb * 4,
                                              0, 0);
   }
@@ -273,14 +275,30 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   v8i a10, a11;
   read_tile(st, pl.va, 1, a10, a11);
   if (S == 0) {
-    // scales of K-blocks kb..kb+2 (landed before the previous barrier)
-    const v4f x0 = *(const v4f*)(pipe_scale + pl.sa0);
-    const v4f x1 = *(const v4f*)(pipe_scale + pl.sa1);
+    // scales of K-blocks kb..kb+2 (landed before the previous barrier): three fp32
+    // values, or (packed) bytes kb % 4 .. kb % 4 + 2 of the words from kb / 4 on
     const v4f b = *(const v4f*)(pipe_sfb + pl.sb);
+    float a0[3], a1[3];
+    if (th.sa_shift) {
+      const uint2 w0 = *(const uint2*)(pipe_scale + pl.sa0);
+      const uint2 w1 = *(const uint2*)(pipe_scale + pl.sa1);
+      const uint64_t q0 = ((uint64_t)w0.y << 32) | w0.x, q1 = ((uint64_t)w1.y << 32) | w1.x;
+      const int o = (kb & 3) * 8;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        a0[j] = ue8m0_value((uint32_t)(q0 >> (o + 8 * j)) & 0xFFu);
+        a1[j] = ue8m0_value((uint32_t)(q1 >> (o + 8 * j)) & 0xFFu);
+      }
+    } else {
+      const v4f x0 = *(const v4f*)(pipe_scale + pl.sa0);
+      const v4f x1 = *(const v4f*)(pipe_scale + pl.sa1);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) a0[j] = x0[j], a1[j] = x1[j];
+    }
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      sc.s0[j] = x0[j] * b[j];
-      sc.s1[j] = x1[j] * b[j];
+      sc.s0[j] = a0[j] * b[j];
+      sc.s1[j] = a1[j] * b[j];
     }
   }
   DG_FENCE();
@@ -355,7 +373,9 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
     // fetches nothing
     th.a_rsrc = raw_rsrc(v.A + v.m0 * K, (int64_t)a_rows * K);
     th.b_rsrc = raw_rsrc(v.B + v.n0 * K, (int64_t)b_rows * K);
-    th.sa_rsrc = raw_rsrc(v.sfA + v.m0 * KB, (v.rows - v.m0) * KB * 4);
+    const int64_t rb = sfa_row_bytes(KB, p.sfa_packed);
+    th.sa_rsrc = raw_rsrc(v.sfA + v.m0 * rb, (v.rows - v.m0) * rb);
+    th.sa_shift = p.sfa_packed ? 2 : 0;
     th.sb_rsrc = raw_rsrc(v.sfB + (int64_t)nb0 * KB, (int64_t)(NB - nb0) * KB * 4);
     const int rsub = lane >> 3, c = lane & 7;
 #pragma unroll
@@ -370,7 +390,7 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
     }
     int arow = wave * Cfg::RPW + (lane % Cfg::RPW);
     if (arow >= a_rows) arow = a_rows - 1;
-    th.sa_off = (uint32_t)arow * (uint32_t)KB * 4u;
+    th.sa_off = (uint32_t)arow * (uint32_t)rb;
     int nb = lane < Cfg::BN / 128 ? lane : Cfg::BN / 128 - 1;
     if (nb0 + nb >= NB) nb = NB - 1 - nb0;
     th.sb_off = (uint32_t)nb * (uint32_t)KB * 4u;
@@ -656,7 +676,7 @@ __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
     v.m0 = (int64_t)tm * Cfg::BM;
     v.n0 = (int64_t)tn * Cfg::BN;
     v.A = p.A + (int64_t)e * p.M * p.K;
-    v.sfA = p.sfA + (int64_t)e * p.M * KB;
+    v.sfA = p.sfA + (int64_t)e * p.M * sfa_row_bytes(KB, p.sfa_packed);
     v.C = p.C + (int64_t)e * p.M * p.N;
     v.B = p.B + (int64_t)e * p.N * p.K;
     v.sfB = p.sfB + (int64_t)e * NB * KB;

@@ -68,14 +68,14 @@ struct SkinnySrc {
   const uint8_t* b_row[Cfg::TN];
   const uint8_t* a_src[Cfg::A_PER];
   int a_dst[Cfg::A_PER];
-  const float* sa_src;
+  const uint8_t* sa_src;  // this lane's sfA row, at K-block kb0
 };
 
-template <class Cfg>
+template <class Cfg, bool PACKED>
 __device__ __forceinline__ void skinny_issue(SkinnyStage<Cfg>& st, const SkinnySrc<Cfg>& src,
                                              int tc) {
   const int64_t off = (int64_t)tc * kKBlock;
-  st.sa = src.sa_src[tc];
+  st.sa = PACKED ? ue8m0_value(src.sa_src[tc]) : ((const float*)src.sa_src)[tc];
 #pragma unroll
   for (int u = 0; u < Cfg::A_PER; ++u) st.a[u] = *(const v4u*)(src.a_src[u] + off);
 #pragma unroll
@@ -121,7 +121,9 @@ __device__ __forceinline__ void skinny_mma(v4f (&acc)[Cfg::TM][Cfg::TN], const u
         acc[i][j][q] = __builtin_fmaf(part[i][j][q], sab[i][q], acc[i][j][q]);
 }
 
-template <class Cfg>
+// PACKED: sfA in the packed UE8M0 layout (a compile-time choice, so that the fp32
+// form carries no trace of it).
+template <class Cfg, bool PACKED>
 __global__ void __launch_bounds__(Cfg::NT) skinny_kernel(SkinnyArgs args) {
   extern __shared__ __align__(16) uint8_t lds[];
   constexpr int TN = Cfg::TN, TM = Cfg::TM, NT = Cfg::NT, BN = Cfg::BN, D = Cfg::D;
@@ -157,12 +159,12 @@ __global__ void __launch_bounds__(Cfg::NT) skinny_kernel(SkinnyArgs args) {
   }
   {
     const int64_t r = lane < M ? lane : M - 1;
-    src.sa_src = p.sfA + r * KB + kb0;
+    src.sa_src = p.sfA + r * sfa_row_bytes(KB, PACKED) + (PACKED ? kb0 : kb0 * 4);
   }
 
   SkinnyStage<Cfg> st[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) skinny_issue<Cfg>(st[j], src, j < ks ? j : ks - 1);
+  for (int j = 0; j < D; ++j) skinny_issue<Cfg, PACKED>(st[j], src, j < ks ? j : ks - 1);
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -182,7 +184,7 @@ __global__ void __launch_bounds__(Cfg::NT) skinny_kernel(SkinnyArgs args) {
       __syncthreads();  // block t's A tile and sfA column are in the slot
       if (t < ks) skinny_mma<Cfg>(acc, slot, st[j].b, sfb[t], g, l16);
       const int tn = t + D;
-      skinny_issue<Cfg>(st[j], src, tn < ks ? tn : ks - 1);
+      skinny_issue<Cfg, PACKED>(st[j], src, tn < ks ? tn : ks - 1);
     }
   }
 

@@ -111,9 +111,9 @@ __device__ __forceinline__ void stream_issue_all(StreamRegs<Cfg>& r, __amdgpu_bu
   }
 }
 
-template <class Cfg, int T>
+template <class Cfg, int T, bool PACKED>
 __device__ __forceinline__ void stream_compute(v4f (&acc)[Cfg::TM][Cfg::TN], const StreamRegs<Cfg>& r,
-                                               int ks, int g, int l16) {
+                                               int ks, int g, int l16, int shift) {
   if constexpr (T < Cfg::D) {
     // this wave's loads of blocks 0..T have landed; every wave's A DMAs of block T
     // are visible after the barrier
@@ -132,7 +132,8 @@ __device__ __forceinline__ void stream_compute(v4f (&acc)[Cfg::TM][Cfg::TN], con
         const v4u hi = *(const v4u*)(rowp + (((g + 4) ^ swz(row)) << 4));
         af[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sa[i] = ((const float*)(stream_sfa + (T / 4) * 1024 + row * 16))[T % 4];
+        sa[i] = PACKED ? ue8m0_value(stream_sfa[row * 16 + shift + T])
+                       : ((const float*)(stream_sfa + (T / 4) * 1024 + row * 16))[T % 4];
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -145,11 +146,12 @@ __device__ __forceinline__ void stream_compute(v4f (&acc)[Cfg::TM][Cfg::TN], con
           for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(part[q], s, acc[i][j][q]);
         }
     }
-    stream_compute<Cfg, T + 1>(acc, r, ks, g, l16);
+    stream_compute<Cfg, T + 1, PACKED>(acc, r, ks, g, l16, shift);
   }
 }
 
-template <class Cfg>
+// PACKED: sfA in the packed UE8M0 layout (compile-time, as in the skinny kernel).
+template <class Cfg, bool PACKED>
 __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
   constexpr int TN = Cfg::TN, TM = Cfg::TM, NT = Cfg::NT, BN = Cfg::BN;
   const Problem& p = args.p;
@@ -193,8 +195,13 @@ __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
   {
     // scale resources end at the arrays' ends: reads past the last K-block give 0
+    // fp32: the run's values start at sfA + kb0; packed: at the word holding K-block
+    // kb0 (byte kb0 % 4 of the staged 16 bytes). Groups past the first hold nothing
+    // the packed form uses; they keep the load count the same.
+    const int64_t rb = sfa_row_bytes(KB, PACKED);
+    const int64_t sa0 = PACKED ? (kb0 & ~3) : (int64_t)kb0 * 4;
     const __amdgpu_buffer_rsrc_t sa_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(p.sfA + kb0), 0, (int)((M * KB - kb0) * 4), 0x00020000);
+        const_cast<uint8_t*>(p.sfA + sa0), 0, (int)(M * rb - sa0), 0x00020000);
     const int NB = (int)((N + kKBlock - 1) / kKBlock);
     const __amdgpu_buffer_rsrc_t sb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(p.sfB + kb0), 0, (int)(((int64_t)NB * KB - kb0) * 4), 0x00020000);
@@ -203,7 +210,7 @@ __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
     for (int c = 0; c < Cfg::SF4; ++c)  // identical bytes from every wave
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           sa_rsrc, (__attribute__((address_space(3))) void*)(stream_sfa + c * 1024), 16,
-          (uint32_t)row * (uint32_t)KB * 4u, c * 16, 0, 0);
+          (uint32_t)row * (uint32_t)rb, c * 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       int nb = (int)((n0 + (wave * TN + j) * 16) / kKBlock);
@@ -223,7 +230,7 @@ __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  stream_compute<Cfg, 0>(acc, r, ks, g, l16);
+  stream_compute<Cfg, 0, PACKED>(acc, r, ks, g, l16, kb0 & 3);
 
   // ---- split reduction. Partials are written and read with device-scope (sc1)
   // 16-byte accesses (measured faster here than L2-resident ones); waiting for every

@@ -110,6 +110,35 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked(const void* A, const void* B, void* C,
                                           int64_t expected_m, void* hip_stream);
 
 /*
+ * The same three calls with sfA in the packed UE8M0 layout, the exponent-only form
+ * of the LHS scaling factors that the project page (aiproducthub.cn, "technical
+ * implementation") names as a way to cut scale traffic. Every sfA value must then be
+ * a power of two 2^(b - 127), b in [0, 254]; the byte b stands for it:
+ *   sfA  uint32 [rows][ceil(K/512)]: byte j (little-endian) of word w in row m is
+ *        b for K-block 4w + j of row m; bytes past K/128 in a row's last word are
+ *        not read. rows = M (dense), M_total (contiguous), G * M_max (masked, as
+ *        [G][M_max][ceil(K/512)]).
+ * A byte of 255 (NaN in the OCP MX format) is not a scale; results are unspecified.
+ * Everything else (other operands, sfB in fp32, errors, untouched rows) is as in the
+ * fp32-scale calls, and with equal scales the outputs are bitwise the same.
+ */
+dg_status dg_fp8_gemm_nt_ue8m0(const void* A, const void* B, void* C, const uint32_t* sfA,
+                               const float* sfB, int64_t M, int64_t N, int64_t K,
+                               void* hip_stream);
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const void* A, const void* B, void* C,
+                                                    const uint32_t* sfA, const float* sfB,
+                                                    const int32_t* m_indices, int64_t M_total,
+                                                    int64_t N, int64_t K, int32_t G,
+                                                    void* hip_stream);
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* A, const void* B, void* C,
+                                                const uint32_t* sfA, const float* sfB,
+                                                const int32_t* masked_m, int32_t G,
+                                                int64_t M_max, int64_t N, int64_t K,
+                                                int64_t expected_m, void* hip_stream);
+
+/*
  * Per-token 1x128 activation quantizer: the step that turns activations into the
  * A operand and sfA of the calls above (one scaling factor per small block, each
  * block then spanning the FP8 range on its own: launch article, section 1.2).

@@ -18,6 +18,8 @@ and the passages of the pages it follows, are stated in that file:
 * ``quantize_blocks``: power-of-two per-block scale and nearest-e4m3fn codes, written
   as a search (launch article section 1.2).
 * ``bf16_rne``: one rounding from fp64 to bf16.
+* ``unpack_ue8m0``: fp32 scales from the packed exponent-byte (UE8M0) layout of the
+  LHS scaling factors -- project page, "technical implementation".
 
 Every function here is pinned by CPU tests against values fixed by the format
 definitions and by closed forms (``tests/test_oracle_*.py``).
@@ -79,6 +81,7 @@ def _load():
     lib.dgo_e4m3fn_nearest.restype = ctypes.c_uint8
     lib.dgo_e4m3fn_nearest.argtypes = [ctypes.c_double]
     lib.dgo_quantize_blocks.argtypes = [_f32p, _i64, _i64, _i64, _i64, _u8p, _f32p]
+    lib.dgo_unpack_ue8m0.argtypes = [ctypes.POINTER(ctypes.c_uint32), _i64, _i64, _f32p]
     lib.dgo_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -214,6 +217,18 @@ def scale_exponent(amax: float) -> int:
 
 def e4m3fn_nearest(y: float) -> int:
     return int(_load().dgo_e4m3fn_nearest(float(y)))
+
+
+def unpack_ue8m0(packed, KB: int) -> np.ndarray:
+    """fp32 scales [..., KB] from packed UE8M0 words [..., ceil(KB/4)] (uint32 or int32)."""
+    packed = np.ascontiguousarray(packed).view(np.uint32)
+    lead = packed.shape[:-1]
+    assert packed.shape[-1] == (KB + 3) // 4
+    rows = int(np.prod(lead)) if lead else 1
+    out = np.empty(lead + (KB,), dtype=np.float32)
+    _load().dgo_unpack_ue8m0(packed.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), rows, KB,
+                             _p(out, _f32p))
+    return out
 
 
 def quantize_blocks(x, br: int, bc: int):

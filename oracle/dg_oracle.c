@@ -311,6 +311,26 @@ void dgo_quantize_blocks(const float* x, int64_t R, int64_t C, int64_t br, int64
   }
 }
 
+/* ------------------------------------------------------------------ UE8M0 scales */
+/*
+ * Packed UE8M0 layout of the LHS scaling factors (DeepGEMM project page,
+ * aiproducthub.cn, "technical implementation": an exponent-only packed layout for
+ * the LHS scales to reduce memory traffic). Reading: each power-of-two scale 2^e is
+ * stored as the unsigned byte e + 127 (the UE8M0 format: an 8-bit exponent, no sign,
+ * no mantissa), four consecutive K-blocks per little-endian 32-bit word, rows padded
+ * to whole words: byte j of word w of a row is K-block 4w + j. Written out: the byte
+ * with value b means 2^(b - 127) (b = 255 is not a scale).
+ */
+void dgo_unpack_ue8m0(const uint32_t* packed, int64_t rows, int64_t KB, float* out) {
+  int64_t words = (KB + 3) / 4, r, kb;
+  for (r = 0; r < rows; ++r)
+    for (kb = 0; kb < KB; ++kb) {
+      uint32_t w = packed[r * words + kb / 4];
+      unsigned b = (w >> (8 * (kb % 4))) & 0xFFu;
+      out[r * KB + kb] = (float)ldexp(1.0, (int)b - 127);
+    }
+}
+
 int dgo_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -99,6 +99,24 @@ def quantize(x: np.ndarray, br: int, bc: int = BLOCK):
     return codes, scales
 
 
+def pack_ue8m0(sf: np.ndarray) -> np.ndarray:
+    """The packed UE8M0 form of power-of-two scales sf [..., KB]: int32 [..., ceil(KB/4)]
+    words whose byte j (little-endian) of word w is e + 127 for the scale 2^e of
+    K-block 4w + j; padding bytes are 0. An input layout, not arithmetic of the method."""
+    sf = np.asarray(sf, dtype=np.float32)
+    m, e = np.frexp(sf.astype(np.float64))
+    if not np.all(m == 0.5):
+        raise ValueError("UE8M0 holds powers of two only")
+    b = e - 1 + 127
+    if b.size and (b.min() < 0 or b.max() > 254):
+        raise ValueError("scale exponent outside the UE8M0 range")
+    KB = sf.shape[-1]
+    words = (KB + 3) // 4
+    out = np.zeros(sf.shape[:-1] + (words * 4,), dtype=np.uint8)
+    out[..., :KB] = b
+    return np.ascontiguousarray(out).view("<i4").reshape(sf.shape[:-1] + (words,))
+
+
 def make_operand(seed: int, R: int, C: int, br: int):
     """Draw N(0,1) R x C (as normal_rows(seed, R, C)) and quantize with br x 128 blocks."""
     assert C % BLOCK == 0 and br in (1, BLOCK)

@@ -159,3 +159,55 @@ def test_quantizer_scale_covariance_and_idempotence():
     deq = (oracle.e4m3fn_values()[codes] * np.repeat(scales, 128, axis=1)).astype(np.float32)
     c3, s3 = oracle.quantize_blocks(deq, 1, 128)
     assert np.array_equal(c3, codes) and np.array_equal(s3, scales)
+
+
+# ------------------------------------------------------------------ UE8M0 scale bytes
+
+
+def test_ue8m0_unpack_every_byte():
+    # byte b means 2^(b - 127): checked against numpy's ldexp and against the fp32 bit
+    # layout (exponent field b for b >= 1, the subnormal 2^-127 = 0x00400000 for b = 0)
+    KB = 255
+    packed = np.zeros((1, (KB + 3) // 4), dtype=np.uint32)
+    for kb in range(KB):
+        packed[0, kb // 4] |= np.uint32(kb) << np.uint32(8 * (kb % 4))
+    got = oracle.unpack_ue8m0(packed, KB)[0]
+    want = np.ldexp(np.float64(1.0), np.arange(KB) - 127).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    bits = got.view(np.uint32)
+    assert bits[0] == 0x00400000
+    assert np.array_equal(bits[1:], np.arange(1, KB, dtype=np.uint32) << np.uint32(23))
+
+
+@pytest.mark.parametrize("KB", [1, 3, 4, 5, 56, 145])
+def test_ue8m0_unpack_layout(KB):
+    # byte j of word w is K-block 4w + j; the padding bytes of a row's last word are
+    # ignored (filled with 255 here, which is not a scale)
+    rng = np.random.default_rng(KB)
+    rows = 3
+    e = rng.integers(-20, 21, size=(rows, KB))
+    words = (KB + 3) // 4
+    b = np.full((rows, words * 4), 255, dtype=np.uint8)
+    b[:, :KB] = (e + 127).astype(np.uint8)
+    packed = b.view("<u4").reshape(rows, words)
+    got = oracle.unpack_ue8m0(packed, KB)
+    assert np.array_equal(got, np.ldexp(1.0, e).astype(np.float32))
+
+
+def test_ue8m0_gemm_equals_fp32_scale_gemm():
+    # the packed form only re-encodes power-of-two scales: the oracle's product is the
+    # same bit for bit
+    rng = np.random.default_rng(5)
+    M, N, K = 5, 144, 640
+    KB = K // 128
+    A = rng.integers(0, 0x7F, size=(M, K), dtype=np.uint8)
+    B = rng.integers(0, 0x7F, size=(N, K), dtype=np.uint8)
+    e = rng.integers(-8, 9, size=(M, KB))
+    sfA = np.ldexp(1.0, e).astype(np.float32)
+    sfB = np.ldexp(1.0, rng.integers(-3, 4, size=((N + 127) // 128, KB))).astype(np.float32)
+    b = np.zeros((M, 8), dtype=np.uint8)
+    b[:, :KB] = e + 127
+    packed = b.view("<u4").reshape(M, 2)
+    r1 = oracle.gemm_nt(A, B, sfA, sfB)
+    r2 = oracle.gemm_nt(A, B, oracle.unpack_ue8m0(packed, KB), sfB)
+    assert np.array_equal(r1.view(np.uint64), r2.view(np.uint64))
