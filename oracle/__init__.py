@@ -18,6 +18,8 @@ and the passages of the pages it follows, are stated in that file:
 * ``quantize_blocks``: power-of-two per-block scale and nearest-e4m3fn codes, written
   as a search (launch article section 1.2).
 * ``bf16_rne``: one rounding from fp64 to bf16.
+* ``swiglu``: h = silu(gate) * up between the two grouped GEMMs of an MoE layer --
+  project page, "core features" (Mega MoE: Linear1, SwiGLU, Linear2 fused).
 * ``unpack_ue8m0``: fp32 scales from the packed exponent-byte (UE8M0) layout of the
   LHS scaling factors -- project page, "technical implementation".
 
@@ -81,6 +83,7 @@ def _load():
     lib.dgo_e4m3fn_nearest.restype = ctypes.c_uint8
     lib.dgo_e4m3fn_nearest.argtypes = [ctypes.c_double]
     lib.dgo_quantize_blocks.argtypes = [_f32p, _i64, _i64, _i64, _i64, _u8p, _f32p]
+    lib.dgo_swiglu.argtypes = [_f64p, _i64, _i64, _f64p]
     lib.dgo_unpack_ue8m0.argtypes = [ctypes.POINTER(ctypes.c_uint32), _i64, _i64, _f32p]
     lib.dgo_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -217,6 +220,17 @@ def scale_exponent(amax: float) -> int:
 
 def e4m3fn_nearest(y: float) -> int:
     return int(_load().dgo_e4m3fn_nearest(float(y)))
+
+
+def swiglu(gu) -> np.ndarray:
+    """h [..., I] = silu(gate) * up in fp64 from gu [..., 2I] (gate = first half)."""
+    gu = np.ascontiguousarray(gu, dtype=np.float64)
+    lead, two_i = gu.shape[:-1], gu.shape[-1]
+    assert two_i % 2 == 0
+    rows = int(np.prod(lead)) if lead else 1
+    h = np.empty(lead + (two_i // 2,), dtype=np.float64)
+    _load().dgo_swiglu(_p(gu, _f64p), rows, two_i // 2, _p(h, _f64p))
+    return h
 
 
 def unpack_ue8m0(packed, KB: int) -> np.ndarray:

@@ -311,6 +311,23 @@ void dgo_quantize_blocks(const float* x, int64_t R, int64_t C, int64_t br, int64
   }
 }
 
+/* ------------------------------------------------------------------ SwiGLU */
+/*
+ * The activation between an MoE layer's two grouped GEMMs (DeepGEMM project page,
+ * aiproducthub.cn, "core features": Mega MoE fuses Linear1, SwiGLU and Linear2).
+ * Reading: Linear1's output row holds the gate half in columns [0, I) and the up
+ * half in [I, 2I); the activation is h[j] = silu(gate[j]) * up[j] with
+ * silu(x) = x / (1 + exp(-x)), in fp64. gu is [rows][2I], h is [rows][I].
+ */
+void dgo_swiglu(const double* gu, int64_t rows, int64_t I, double* h) {
+  int64_t r, j;
+  for (r = 0; r < rows; ++r)
+    for (j = 0; j < I; ++j) {
+      double g = gu[r * 2 * I + j], u = gu[r * 2 * I + I + j];
+      h[r * I + j] = g / (1.0 + exp(-g)) * u;
+    }
+}
+
 /* ------------------------------------------------------------------ UE8M0 scales */
 /*
  * Packed UE8M0 layout of the LHS scaling factors (DeepGEMM project page,

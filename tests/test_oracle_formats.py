@@ -211,3 +211,50 @@ def test_ue8m0_gemm_equals_fp32_scale_gemm():
     r1 = oracle.gemm_nt(A, B, sfA, sfB)
     r2 = oracle.gemm_nt(A, B, oracle.unpack_ue8m0(packed, KB), sfB)
     assert np.array_equal(r1.view(np.uint64), r2.view(np.uint64))
+
+
+# ------------------------------------------------------------------ SwiGLU
+
+
+def _gu(g, u):
+    g, u = np.atleast_2d(np.asarray(g, np.float64)), np.atleast_2d(np.asarray(u, np.float64))
+    return np.concatenate([g, u], axis=-1)
+
+
+def test_swiglu_closed_forms():
+    # silu(0) = 0; silu(x) -> x for large x, -> 0 for very negative x; h scales with up
+    h = oracle.swiglu(_gu([0.0, 40.0, -800.0, 1.0], [5.0, 1.0, 3.0, 2.0]))[0]
+    assert h[0] == 0.0
+    assert h[1] == 40.0  # exp(-40) < 2^-57: 40 / (1 + tiny) rounds to 40
+    assert h[2] == 0.0 or abs(h[2]) < 1e-300
+    # 1 / (1 + e^-1) is the logistic value at 1
+    assert abs(h[3] - 2.0 / (1.0 + math.e ** -1)) <= 4e-16
+
+
+def test_swiglu_identities():
+    rng = np.random.default_rng(3)
+    g = rng.normal(0, 6, 4096)
+    one = np.ones_like(g)
+    hp = oracle.swiglu(_gu(g, one))[0]
+    hm = oracle.swiglu(_gu(-g, one))[0]
+    # silu(x) - silu(-x) = x, since sigmoid(x) + sigmoid(-x) = 1
+    assert np.allclose(hp - hm, g, rtol=0, atol=1e-13 * (1 + np.abs(g)))
+    # other closed forms, through other library routines: x/2 (1 + tanh(x/2)) where it
+    # does not cancel (x >= -1), x e^x / (1 + e^x) below
+    t = np.array([x / 2 * (1 + math.tanh(x / 2)) if x >= -1 else
+                  x * math.exp(x) / (1 + math.exp(x)) for x in g])
+    assert np.allclose(hp, t, rtol=1e-14, atol=1e-300)
+    # linear in up, exactly for powers of two
+    u = rng.normal(size=g.size)
+    h1 = oracle.swiglu(_gu(g, u))[0]
+    h2 = oracle.swiglu(_gu(g, 4 * u))[0]
+    assert np.array_equal(h2, 4 * h1)
+
+
+def test_swiglu_layout_halves():
+    # gate is the first half of each row, up the second; rows are independent
+    gu = np.array([[1.0, 2.0, 10.0, 20.0], [3.0, 0.0, 1.0, 7.0]])
+    h = oracle.swiglu(gu)
+    assert h.shape == (2, 2)
+    assert h[0, 0] == 1.0 / (1.0 + math.exp(-1.0)) * 10.0
+    assert h[1, 1] == 0.0
