@@ -12,6 +12,8 @@ article, deepseek.csdn.net, section 4.2 "advanced tuning"):
 * ``m_grouped_fp8_gemm_nt_contiguous(a, b, c, a_sf, b_sf, m_indices)``
 * ``m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None)``
 * ``quantize_fp8_1x128(x, codes=None, sf=None)``: activations -> (A codes, sfA)
+* ``m_grouped_fp8_gemm_nt_{contiguous,masked}_swiglu(...)``: Linear1 with a fused
+  SwiGLU + requantization epilogue -> (codes, sf) of h = silu(gate) * up
 
 Operands: ``a``/``b`` are ``torch.float8_e4m3fn`` (``torch.uint8`` holding e4m3fn
 codes is accepted too), ``a_sf``/``b_sf`` ``torch.float32``, ``c`` ``torch.bfloat16``
@@ -60,6 +62,12 @@ lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.argtypes = \
     lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes
 lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.restype = ctypes.c_int
 lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes
+lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu.restype = ctypes.c_int
+lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                          _i64, _i64, _i64, _i32, _vp]
+lib.dg_m_grouped_fp8_gemm_nt_masked_swiglu.restype = ctypes.c_int
+lib.dg_m_grouped_fp8_gemm_nt_masked_swiglu.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                      _i64, _i64, _i64, _vp]
 lib.dg_quantize_fp8_1x128.restype = ctypes.c_int
 lib.dg_quantize_fp8_1x128.argtypes = [_vp, _i32, _vp, _vp, _i64, _i64, _vp]
 
@@ -190,6 +198,66 @@ def m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None)
             masked_m.data_ptr(), G, M_max, N, K, em, _stream(dev)))
 
 
+def _swiglu_outputs(lead: tuple, I: int, codes, sf, dev):
+    if codes is None:
+        codes = torch.empty(lead + (I,), dtype=torch.float8_e4m3fn, device=dev)
+    if sf is None:
+        sf = torch.empty(lead + (I // BLOCK,), dtype=torch.float32, device=dev)
+    _fp8(codes, "codes")
+    _need(codes, "codes", codes.dtype, lead + (I,), dev)
+    _need(sf, "sf", torch.float32, lead + (I // BLOCK,), dev)
+    return codes, sf
+
+
+def m_grouped_fp8_gemm_nt_contiguous_swiglu(a, b, a_sf, b_sf, m_indices, codes=None, sf=None):
+    """Contiguous MoE Linear1 with the fused SwiGLU + 1x128 requantization epilogue.
+    b is [G, 2I, K] (gate rows, then up rows); returns (codes [M_total, I] e4m3fn,
+    sf [M_total, I/128] fp32) of h = silu(gate) * up, written into the given tensors
+    when passed. Pad rows are not written."""
+    _fp8(a, "a"), _fp8(b, "b")
+    if a.dim() != 2 or b.dim() != 3 or b.shape[1] % 2:
+        raise ValueError("a must be [M_total, K] and b [G, 2I, K]")
+    M, K = a.shape
+    G, N2 = b.shape[0], b.shape[1]
+    I = N2 // 2
+    dev = a.device
+    _dev(a, "a", dev)
+    _need(b, "b", b.dtype, (G, N2, K), dev)
+    _need(a_sf, "a_sf", torch.float32, (M, K // BLOCK), dev)
+    _need(b_sf, "b_sf", torch.float32, (G, N2 // BLOCK, K // BLOCK), dev)
+    _need(m_indices, "m_indices", torch.int32, (M,), dev)
+    codes, sf = _swiglu_outputs((M,), I, codes, sf, dev)
+    with torch.cuda.device(dev):
+        check(lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(
+            a.data_ptr(), b.data_ptr(), codes.data_ptr(), sf.data_ptr(), a_sf.data_ptr(),
+            b_sf.data_ptr(), m_indices.data_ptr(), M, I, K, G, _stream(dev)))
+    return codes, sf
+
+
+def m_grouped_fp8_gemm_nt_masked_swiglu(a, b, a_sf, b_sf, masked_m, codes=None, sf=None):
+    """Masked MoE Linear1 with the fused SwiGLU + 1x128 requantization epilogue:
+    returns (codes [G, M_max, I], sf [G, M_max, I/128]); rows >= masked_m[e] are not
+    written."""
+    _fp8(a, "a"), _fp8(b, "b")
+    if a.dim() != 3 or b.dim() != 3 or b.shape[1] % 2:
+        raise ValueError("a must be [G, M_max, K] and b [G, 2I, K]")
+    G, M_max, K = a.shape
+    N2 = b.shape[1]
+    I = N2 // 2
+    dev = a.device
+    _dev(a, "a", dev)
+    _need(b, "b", b.dtype, (G, N2, K), dev)
+    _need(a_sf, "a_sf", torch.float32, (G, M_max, K // BLOCK), dev)
+    _need(b_sf, "b_sf", torch.float32, (G, N2 // BLOCK, K // BLOCK), dev)
+    _need(masked_m, "masked_m", torch.int32, (G,), dev)
+    codes, sf = _swiglu_outputs((G, M_max), I, codes, sf, dev)
+    with torch.cuda.device(dev):
+        check(lib.dg_m_grouped_fp8_gemm_nt_masked_swiglu(
+            a.data_ptr(), b.data_ptr(), codes.data_ptr(), sf.data_ptr(), a_sf.data_ptr(),
+            b_sf.data_ptr(), masked_m.data_ptr(), G, M_max, I, K, _stream(dev)))
+    return codes, sf
+
+
 def quantize_fp8_1x128(x, codes=None, sf=None):
     """Per-token 1x128 quantization of x [M, K] (float32 or bfloat16): returns
     (codes [M, K] torch.float8_e4m3fn, sf [M, K/128] torch.float32), written into the
@@ -229,4 +297,5 @@ def config_names() -> list[str]:
 
 
 __all__ = ["config_names", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+           "m_grouped_fp8_gemm_nt_contiguous_swiglu", "m_grouped_fp8_gemm_nt_masked_swiglu",
            "quantize_fp8_1x128", "describe_config", "DGError", "lib", "LIB_PATH"]

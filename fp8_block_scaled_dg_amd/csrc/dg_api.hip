@@ -125,6 +125,31 @@ dg_status launch_pipe(const Problem& p0, int64_t blocks, hipStream_t stream) {
 using Pipe256x128 = PipeCfg<256, 128>;
 using Pipe128x256 = PipeCfg<128, 256>;
 
+// Grouped GEMM with the fused SwiGLU epilogue: p.N = 2 * I rows of B per expert
+// ([gate; up]); one 128x256 tile per 128 columns of h.
+template <int KIND>
+dg_status launch_pipe_swiglu(const Problem& p0, int64_t blocks, int64_t I, uint8_t* codes,
+                             float* sf, hipStream_t stream) {
+  using Cfg = Pipe128x256;
+  PipeArgs a{};
+  a.p = p0;
+  a.p.tiles_m = (int32_t)((p0.M + Cfg::BM - 1) / Cfg::BM);
+  a.p.tiles_n = (int32_t)(I / 128);
+  const int64_t grid = blocks * a.p.tiles_m * a.p.tiles_n;
+  if (grid <= 0) return DG_OK;
+  if (grid > 0x7FFFFFFF) return fail(DG_ERR_UNSUPPORTED_SHAPE, "grid of %lld tiles", (long long)grid);
+  a.full_tiles = (int32_t)grid;
+  a.parts = 1;
+  a.sw.codes = codes;
+  a.sw.sf = sf;
+  a.sw.I = (int32_t)I;
+  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND, true>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
+                     a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
+  return DG_OK;
+}
+
 // ---------------------------------------------------------------- split-K workspace
 //
 // Skinny launches with K split across workgroups keep fp32 partials and per-tile
@@ -584,6 +609,79 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* A, const void* B, vo
                                                 int64_t M_max, int64_t N, int64_t K,
                                                 int64_t expected_m, void* stream) {
   return gemm_masked(A, B, C, sfA, 1, sfB, masked_m, G, M_max, N, K, expected_m, stream);
+}
+
+}  // extern "C"
+
+namespace dg {
+namespace {
+
+dg_status check_swiglu(const void* A, const void* B, const void* codes, const float* sf,
+                       const float* sfA, const float* sfB, const int32_t* idx, int64_t rows,
+                       int64_t I, int64_t K, int32_t G) {
+  if (rows < 0 || I < 0 || K < 0) return fail(DG_ERR_BAD_SHAPE, "negative size");
+  if (G < 1) return fail(DG_ERR_BAD_SHAPE, "G=%d, need at least one expert", G);
+  if (I % 128 != 0) return fail(DG_ERR_BAD_SHAPE, "I=%lld is not a multiple of 128", (long long)I);
+  if (K % kKBlock != 0) return fail(DG_ERR_BAD_SHAPE, "K=%lld is not a multiple of 128", (long long)K);
+  if (rows == 0 || I == 0) return DG_OK;
+  if (K == 0) return fail(DG_ERR_BAD_SHAPE, "K=0 with outputs to produce");
+  if (!A || !B || !codes || !sf || !sfA || !sfB || !idx)
+    return fail(DG_ERR_NULL_POINTER, "NULL operand pointer");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(codes, 16))
+    return fail(DG_ERR_MISALIGNED, "A, B and codes must be 16-byte aligned");
+  if (!aligned(sf, 4) || !aligned(sfA, 4) || !aligned(sfB, 4) || !aligned(idx, 4))
+    return fail(DG_ERR_MISALIGNED, "scales and index arrays must be 4-byte aligned");
+  if (K / kKBlock > kPipeMaxKB || (I + 256) * K >= ((int64_t)1 << 31) || rows > ((int64_t)1 << 30))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "(I + 256) * K must stay below 2^31");
+  return DG_OK;
+}
+
+}  // namespace
+}  // namespace dg
+
+extern "C" {
+
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(const void* A, const void* B, void* codes,
+                                                     float* sf, const float* sfA,
+                                                     const float* sfB, const int32_t* m_indices,
+                                                     int64_t M_total, int64_t I, int64_t K,
+                                                     int32_t G, void* stream) {
+  g_detail[0] = 0;
+  dg_status s = check_swiglu(A, B, codes, sf, sfA, sfB, m_indices, M_total, I, K, G);
+  if (s != DG_OK || M_total == 0 || I == 0) return s;
+  Problem p{};
+  p.A = (const uint8_t*)A;
+  p.B = (const uint8_t*)B;
+  p.sfA = (const uint8_t*)sfA;
+  p.sfB = sfB;
+  p.m_indices = m_indices;
+  p.M = M_total;
+  p.N = 2 * I;
+  p.K = K;
+  p.G = G;
+  return launch_pipe_swiglu<kContiguous>(p, 1, I, (uint8_t*)codes, sf, (hipStream_t)stream);
+}
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked_swiglu(const void* A, const void* B, void* codes,
+                                                 float* sf, const float* sfA, const float* sfB,
+                                                 const int32_t* masked_m, int32_t G,
+                                                 int64_t M_max, int64_t I, int64_t K,
+                                                 void* stream) {
+  g_detail[0] = 0;
+  dg_status s = check_swiglu(A, B, codes, sf, sfA, sfB, masked_m, M_max, I, K, G);
+  if (s != DG_OK || M_max == 0 || I == 0) return s;
+  if ((int64_t)G * M_max > (int64_t)1 << 34) return fail(DG_ERR_UNSUPPORTED_SHAPE, "G*M_max too large");
+  Problem p{};
+  p.A = (const uint8_t*)A;
+  p.B = (const uint8_t*)B;
+  p.sfA = (const uint8_t*)sfA;
+  p.sfB = sfB;
+  p.masked_m = masked_m;
+  p.M = M_max;
+  p.N = 2 * I;
+  p.K = K;
+  p.G = G;
+  return launch_pipe_swiglu<kMasked>(p, G, I, (uint8_t*)codes, sf, (hipStream_t)stream);
 }
 
 dg_status dg_quantize_fp8_1x128(const void* x, int32_t x_dtype, void* codes, float* sf,

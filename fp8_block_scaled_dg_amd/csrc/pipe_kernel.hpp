@@ -38,6 +38,7 @@
 #pragma once
 
 #include "gemm_kernel.hpp"
+#include "quant_kernel.hpp"
 
 namespace dg {
 
@@ -352,9 +353,12 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
 // columns at or past N read as zero (the buffer resources end there). With ACT false
 // the wave only moves its share of the tile's operands and leaves acc at zero: the
 // caller passes false to a wave whose 64 x 64 sub-tile holds nothing to store.
+// b_hi: tile rows from 128 on come from B rows b_hi further on (and their sfB blocks
+// likewise): the up half of a [gate; up] B, b_hi = I - 128. 0 for a plain tile.
 template <class Cfg, bool ACT>
 __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileView& v, int kb_lo,
-                                                 int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN]) {
+                                                 int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN],
+                                                 int b_hi) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR addresses
@@ -372,7 +376,7 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
     // rows past the ends are out of the resources' range: the DMA writes zeros and
     // fetches nothing
     th.a_rsrc = raw_rsrc(v.A + v.m0 * K, (int64_t)a_rows * K);
-    th.b_rsrc = raw_rsrc(v.B + v.n0 * K, (int64_t)b_rows * K);
+    th.b_rsrc = raw_rsrc(v.B + v.n0 * K, (int64_t)(b_hi ? Cfg::BN + b_hi : b_rows) * K);
     const int64_t rb = sfa_row_bytes(KB, p.sfa_packed);
     th.sa_rsrc = raw_rsrc(v.sfA + v.m0 * rb, (v.rows - v.m0) * rb);
     th.sa_shift = p.sfa_packed ? 2 : 0;
@@ -386,12 +390,14 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
 #pragma unroll
     for (int q = 0; q < Cfg::B_DMA; ++q) {
       const int R = (wave * Cfg::B_DMA + q) * 8 + rsub;
-      th.b_off[q] = (uint32_t)R * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+      const int Rg = R + (R >= 128 ? b_hi : 0);  // row of B (relative to n0)
+      th.b_off[q] = (uint32_t)Rg * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
     }
     int arow = wave * Cfg::RPW + (lane % Cfg::RPW);
     if (arow >= a_rows) arow = a_rows - 1;
     th.sa_off = (uint32_t)arow * (uint32_t)rb;
     int nb = lane < Cfg::BN / 128 ? lane : Cfg::BN / 128 - 1;
+    if (nb >= 1) nb += b_hi / 128;
     if (nb0 + nb >= NB) nb = NB - 1 - nb0;
     th.sb_off = (uint32_t)nb * (uint32_t)KB * 4u;
   }
@@ -450,14 +456,14 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
 template <class Cfg>
 __device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& v, int kb_lo,
                                               int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN],
-                                              bool any_row = true) {
+                                              bool any_row = true, int b_hi = 0) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const bool act = any_row && v.m0 + wm * 64 < v.rows && v.n0 + wn * 64 < p.N;
   if (act)
-    pipe_mainloop_as<Cfg, true>(p, v, kb_lo, kb_hi, acc);
+    pipe_mainloop_as<Cfg, true>(p, v, kb_lo, kb_hi, acc, b_hi);
   else
-    pipe_mainloop_as<Cfg, false>(p, v, kb_lo, kb_hi, acc);
+    pipe_mainloop_as<Cfg, false>(p, v, kb_lo, kb_hi, acc, b_hi);
 }
 
 // bf16 RNE store of a finished tile: produced rows (< valid_rows, and for the
@@ -495,12 +501,120 @@ __device__ __forceinline__ void pipe_store(const Problem& p, const TileView& v, 
   }
 }
 
+// Where the fused SwiGLU epilogue writes: e4m3fn codes [rows][I] and fp32 scales
+// [rows][I/128] of h = silu(gate) * up (rows as in the GEMM's A).
+struct SwigluOut {
+  uint8_t* codes;
+  float* sf;
+  int32_t I;
+};
+
+// Fused epilogue of a [gate; up] tile (BM = 128, BN = 256: tile columns 0..127 are
+// gate columns n0.., 128..255 the up columns I + n0..). The activation between an
+// MoE layer's two grouped GEMMs (DeepGEMM project page, aiproducthub.cn, "core
+// features": Mega MoE fuses Linear1, SwiGLU and Linear2) is formed from the fp32
+// accumulators and quantized per 1x128 block (h's columns n0..n0+127 of a row are one
+// block) by the same rule as the activation quantizer, so the output is the next
+// GEMM's A and sfA:
+//   1. the up waves (wn = 2, 3) hand their 64x64 fp32 sub-tiles to the gate waves
+//      with the same lanes (wn - 2) through LDS (the stages are free by now);
+//   2. the gate waves form h = g / (1 + e^-g) * u in fp32 and each row's max |h| over
+//      their 64 columns; the two gate waves of a row half combine theirs through LDS;
+//   3. codes of h * 2^-e go to an LDS tile, the scale 2^e straight to sf;
+//   4. all threads store the tile's produced rows with 16-byte stores.
 template <class Cfg, int KIND>
+__device__ __forceinline__ void pipe_store_swiglu(const Problem& p, const TileView& v, int expert,
+                                                  int valid_rows,
+                                                  v16f (&acc)[Cfg::TM][Cfg::TN],
+                                                  const SwigluOut& out) {
+  static_assert(Cfg::BM == 128 && Cfg::BN == 256, "gate and up halves of 128 columns");
+  constexpr int TM = Cfg::TM, TN = Cfg::TN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const int r32 = lane & 31, g = lane >> 5;
+  const int slot = wm * 2 + (wn & 1);
+  float* xch = (float*)((slot < 2 ? pipe_stage0 : pipe_stage1) + (slot & 1) * 16384);
+  float* rmax_lds = (float*)pipe_scale;   // [wm * 2 + wn][64 rows]
+  uint8_t* codes_lds = pipe_stage2;       // [128 rows][128 columns]
+  if (wn >= 2) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xch[((i * TN + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+  }
+  __syncthreads();
+  if (wn < 2) {
+    float rm[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      rm[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float gt = acc[i][j][e], up = xch[((i * TN + j) * 16 + e) * 64 + lane];
+          const float h = gt / (1.f + expf(-gt)) * up;
+          acc[i][j][e] = h;
+          rm[i] = fmaxf(rm[i], fabsf(h));
+        }
+      rm[i] = fmaxf(rm[i], __shfl_xor(rm[i], 32, 64));
+      if (g == 0) rmax_lds[(wm * 2 + wn) * 64 + i * 32 + r32] = rm[i];
+    }
+  }
+  __syncthreads();
+  if (wn < 2) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rl = wm * 64 + i * 32 + r32;  // row within the tile
+      const float m = fmaxf(rmax_lds[(wm * 2) * 64 + i * 32 + r32],
+                            rmax_lds[(wm * 2 + 1) * 64 + i * 32 + r32]);
+      const int e = quant_scale_exp(m);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            w |= quant_e4m3fn(ldexpf(acc[i][j][4 * q + t], -e)) << (8 * t);
+          *(uint32_t*)(codes_lds + rl * 128 + wn * 64 + j * 32 + 8 * q + 4 * g) = w;
+        }
+      if (wn == 0 && g == 0) {
+        const int64_t row = v.m0 + rl;
+        bool ok = row < (int64_t)valid_rows;
+        if (KIND == kContiguous && ok) ok = p.m_indices[row] == expert;
+        if (ok) out.sf[row * (out.I / 128) + v.n0 / 128] = ldexpf(1.f, e);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = tid; c < 128 * 8; c += Cfg::NT) {
+    const int rl = c >> 3, ch = c & 7;
+    const int64_t row = v.m0 + rl;
+    bool ok = row < (int64_t)valid_rows;
+    if (KIND == kContiguous && ok) ok = p.m_indices[row] == expert;
+    if (ok)
+      *(uint4*)(out.codes + row * out.I + v.n0 + ch * 16) = *(const uint4*)(codes_lds + rl * 128 + ch * 16);
+  }
+  __syncthreads();  // the LDS is free again (the contiguous layout may run another pass)
+}
+
+template <class Cfg, int KIND, bool SWIGLU = false>
 __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, int expert,
-                                          int valid_rows, bool any_row = true) {
+                                          int valid_rows, bool any_row = true,
+                                          SwigluOut sw = SwigluOut{}) {
   v16f acc[Cfg::TM][Cfg::TN];
-  pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, any_row);
-  pipe_store<Cfg, KIND>(p, v, expert, valid_rows, acc);
+  if constexpr (SWIGLU) {
+    pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, any_row, sw.I - 128);
+    pipe_store_swiglu<Cfg, KIND>(p, v, expert, valid_rows, acc, sw);
+  } else {
+    pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, any_row);
+    pipe_store<Cfg, KIND>(p, v, expert, valid_rows, acc);
+  }
 }
 
 // Masked layout: live tile `b` of the schedule that lists, expert by expert, the
@@ -565,6 +679,7 @@ struct PipeArgs {
   uint32_t* counters;  // split tail: one per tile, zero between calls
   int32_t full_tiles;  // dense: tiles computed whole (the first of the tile order)
   int32_t parts;       // dense: K parts of each remaining tile
+  SwigluOut sw;        // fused SwiGLU epilogue (grouped layouts): outputs and I
 };
 
 // Dense tail tile: K-blocks [kb_lo, kb_hi) of tile `tt` (index among the split
@@ -641,8 +756,13 @@ __device__ __forceinline__ void pipe_split_tile(const PipeArgs& a, const TileVie
   pipe_store<Cfg, kDense>(a.p, v, 0, (int)a.p.M, sum);
 }
 
-template <class Cfg, int KIND>
+// SWIGLU (grouped layouts, 128x256 tiles): B is [gate; up] with 2 * sw.I rows per
+// expert, tile tn covers gate columns 128 tn.. and the matching up columns, and the
+// fused epilogue writes quantized h instead of bf16 C.
+template <class Cfg, int KIND, bool SWIGLU = false>
 __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
+  static_assert(!SWIGLU || KIND != kDense, "the fused epilogue is for the grouped layouts");
+  constexpr int NSTEP = SWIGLU ? 128 : Cfg::BN;  // columns between consecutive N-tiles
   const Problem& p = args.p;
   if (KIND == kDense && (int)blockIdx.x >= args.full_tiles) {
     const int h = (int)blockIdx.x - args.full_tiles;
@@ -674,20 +794,23 @@ __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
     const int e = mt.expert, valid = mt.valid;
     grouped_tile<Cfg::GROUP_M>(mt.local, (valid + Cfg::BM - 1) / Cfg::BM, p.tiles_n, tm, tn);
     v.m0 = (int64_t)tm * Cfg::BM;
-    v.n0 = (int64_t)tn * Cfg::BN;
+    v.n0 = (int64_t)tn * NSTEP;
     v.A = p.A + (int64_t)e * p.M * p.K;
     v.sfA = p.sfA + (int64_t)e * p.M * sfa_row_bytes(KB, p.sfa_packed);
     v.C = p.C + (int64_t)e * p.M * p.N;
     v.B = p.B + (int64_t)e * p.N * p.K;
     v.sfB = p.sfB + (int64_t)e * NB * KB;
     v.rows = valid;  // rows past masked_m are never read
-    pipe_tile<Cfg, KIND>(p, v, e, valid);
+    SwigluOut sw = args.sw;  // this expert's rows of the fused epilogue's outputs
+    sw.codes += (int64_t)e * p.M * sw.I;
+    sw.sf += (int64_t)e * p.M * (sw.I / 128);
+    pipe_tile<Cfg, KIND, SWIGLU>(p, v, e, valid, true, sw);
     return;
   }
   const int t = xcd_tile_order(blockIdx.x, KIND == kDense ? args.full_tiles : gridDim.x);
   grouped_tile<Cfg::GROUP_M>(t, p.tiles_m, p.tiles_n, tm, tn);
   v.m0 = (int64_t)tm * Cfg::BM;
-  v.n0 = (int64_t)tn * Cfg::BN;
+  v.n0 = (int64_t)tn * NSTEP;
   v.A = p.A;
   v.sfA = p.sfA;
   v.C = p.C;
@@ -724,7 +847,7 @@ __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
     const bool any_row = __builtin_amdgcn_readfirstlane(s_half[wm]) == e;
     v.B = p.B + (int64_t)e * p.N * p.K;
     v.sfB = p.sfB + (int64_t)e * NB * KB;
-    pipe_tile<Cfg, KIND>(p, v, e, (int)p.M, any_row);
+    pipe_tile<Cfg, KIND, SWIGLU>(p, v, e, (int)p.M, any_row, args.sw);
     prev = e;
   }
 }

@@ -139,6 +139,39 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* A, const void* B, vo
                                                 int64_t expected_m, void* hip_stream);
 
 /*
+ * Grouped GEMM with a fused SwiGLU + requantization epilogue: the first GEMM of an
+ * MoE layer (Linear1) together with the activation between it and the second (the
+ * DeepGEMM project page, aiproducthub.cn, "core features": Mega MoE fuses Linear1,
+ * SwiGLU and Linear2). Per expert, B holds the gate projection in rows [0, I) and the
+ * up projection in rows [I, 2I):
+ *   A      e4m3fn [rows][K]            sfA  fp32 [rows][K/128]
+ *   B      e4m3fn [G][2I][K]           sfB  fp32 [G][2I/128][K/128]
+ *   codes  e4m3fn [rows][I] (output)   sf   fp32 [rows][I/128] (output)
+ * with rows = M_total (contiguous, m_indices as in the contiguous GEMM) or G * M_max
+ * (masked, as [G][M_max][...], masked_m as in the masked GEMM). For each produced
+ * row, with g and u the fp32 block-scaled products of the gate and up columns
+ * (two-level accumulation as in the GEMM calls):
+ *   h[j] = silu(g[j]) * u[j],  silu(x) = x / (1 + e^-x), in fp32;
+ * then h is quantized per 1x128 block exactly as dg_quantize_fp8_1x128 quantizes its
+ * input: these outputs are the next GEMM's A operand and sfA. Rows that are not
+ * produced (pad rows, rows >= masked_m[e]) are not written in codes or sf.
+ * I % 128 == 0; A, B and codes 16-byte aligned, the scale and index arrays 4-byte
+ * aligned; K/128 <= 32768 and (I + 256) * K < 2^31. Stream, ownership and error
+ * conventions as above.
+ */
+dg_status dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(const void* A, const void* B, void* codes,
+                                                     float* sf, const float* sfA,
+                                                     const float* sfB, const int32_t* m_indices,
+                                                     int64_t M_total, int64_t I, int64_t K,
+                                                     int32_t G, void* hip_stream);
+
+dg_status dg_m_grouped_fp8_gemm_nt_masked_swiglu(const void* A, const void* B, void* codes,
+                                                 float* sf, const float* sfA, const float* sfB,
+                                                 const int32_t* masked_m, int32_t G,
+                                                 int64_t M_max, int64_t I, int64_t K,
+                                                 void* hip_stream);
+
+/*
  * Per-token 1x128 activation quantizer: the step that turns activations into the
  * A operand and sfA of the calls above (one scaling factor per small block, each
  * block then spanning the FP8 range on its own: launch article, section 1.2).

@@ -150,3 +150,18 @@ def test_quantizer_binding_checks_dtype_and_device(dg):
         dg.quantize_fp8_1x128(torch.zeros(2, 128, dtype=torch.float16, device="cpu"))
     with pytest.raises(ValueError):
         dg.quantize_fp8_1x128(torch.zeros(2, 128, dtype=torch.float32, device="cpu"))
+
+
+def test_swiglu_calls_reject_bad_arguments(dg):
+    c = dg.lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu
+    m = dg.lib.dg_m_grouped_fp8_gemm_nt_masked_swiglu
+    F = FAKE
+    assert status(dg, c(F, F, F, F, F, F, F, 128, 200, 256, 4, None)) == "DG_ERR_BAD_SHAPE"
+    assert status(dg, c(F, F, F, F, F, F, F, 128, 256, 200, 4, None)) == "DG_ERR_BAD_SHAPE"
+    assert status(dg, c(F, F, None, F, F, F, F, 128, 256, 256, 4, None)) == "DG_ERR_NULL_POINTER"
+    assert status(dg, c(F, F, F + 4, F, F, F, F, 128, 256, 256, 4, None)) == "DG_ERR_MISALIGNED"
+    assert status(dg, c(F, F, F, F, F, F, F, 128, 1 << 20, 1 << 12, 4, None)) == \
+        "DG_ERR_UNSUPPORTED_SHAPE"
+    assert status(dg, m(F, F, F, F, F, F, None, 4, 64, 256, 256, None)) == "DG_ERR_NULL_POINTER"
+    assert status(dg, m(F, F, F, F, F, F, F, 0, 64, 256, 256, None)) == "DG_ERR_BAD_SHAPE"
+    assert status(dg, c(None, None, None, None, None, None, None, 0, 256, 256, 4, None)) == "DG_OK"
