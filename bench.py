@@ -50,6 +50,7 @@ WORKLOADS = {
     "moe_mask": ["moe_mask"],
     "small": ["small"],
     "quant": ["quant_act"],
+    "moe_swiglu": ["moe_cont_swiglu"],
 }
 DESCRIPTIONS = {
     "decode": "dense NT decode, M=64: 64x2112x7168 + 64x32768x512",
@@ -60,6 +61,9 @@ DESCRIPTIONS = {
     "quant": "per-token 1x128 FP8 quantization of bf16 activations [4096][18432] "
              "(the prefill GEMM's A operand and sfA)",
 }
+DESCRIPTIONS["moe_swiglu"] = ("MoE grouped contiguous Linear1 with the fused SwiGLU + 1x128 "
+                              "requantization epilogue: 32 experts, B = [gate; up] with I = 2048, "
+                              "K=7168, 8192 Zipf-routed tokens")
 QUANT_SHAPES = {"quant_act": (4096, 18432, 3001)}  # M, K, seed of the N(0,1) rows
 
 
@@ -137,6 +141,70 @@ class Gemm:
         else:
             dg.m_grouped_fp8_gemm_nt_masked(s["A"], s["B"], s["C"], s["sfA"], s["sfB"], s["idx"],
                                             int(self.w.masked_m.mean()))
+
+
+class SwigluGemm(Gemm):
+    """The contiguous MoE workload as Linear1 of a layer (B = [gate; up], I = N/2) with
+    the fused epilogue: outputs e4m3fn codes [M_total][I] and fp32 scales [M_total][I/128]
+    instead of bf16 C."""
+
+    def __init__(self, name, w, sfa_layout: str = "f32"):
+        super().__init__(name, w)
+        M, N, K = self.shape["M"], self.shape["N"], self.shape["K"]
+        Mv = self.shape["valid_rows"]
+        self.I = N // 2
+        # bf16 C replaced by codes (1 byte) and scales (4 bytes per 128 values)
+        self.bytes += -2 * Mv * N + Mv * self.I + 4 * Mv * (self.I // 128)
+        self.footprint += -M * N * 2 + M * self.I * 5 // 4
+
+    def upload(self, copies: int, sfa_layout: str = "f32"):
+        import torch
+        super().upload(copies, "f32")
+        M = self.shape["M"]
+        for st in self.sets:
+            del st["C"]
+            st["codes"] = torch.empty((M, self.I), dtype=torch.float8_e4m3fn, device="cuda:0")
+            st["sf"] = torch.empty((M, self.I // 128), dtype=torch.float32, device="cuda:0")
+
+    def launch(self, i: int):
+        import fp8_block_scaled_dg_amd as dg
+        s = self.sets[i % len(self.sets)]
+        dg.m_grouped_fp8_gemm_nt_contiguous_swiglu(s["A"], s["B"], s["sfA"], s["sfB"], s["idx"],
+                                                   s["codes"], s["sf"])
+
+
+def swiglu_oracle_leg(g, last_set: int, budget_macs: float = 4e9):
+    """Oracle chain (grouped products, fp64 SwiGLU, quantizer) on seeded whole rows,
+    timed and scaled to every produced row; the last timed step's codes and scales at
+    those rows are compared with it (the kernel forms h in fp32, so a code may differ
+    where h sits within its error of a rounding boundary)."""
+    import numpy as np
+    import torch
+    import oracle
+    w, I = g.w, g.I
+    N2, K = g.shape["N"], g.shape["K"]
+    rows = np.nonzero(w.m_indices >= 0)[0]
+    n_rows = rows.size
+    take = int(min(n_rows, max(1, budget_macs // (N2 * K))))
+    rows = np.sort(np.random.default_rng(12345).choice(rows, take, replace=False))
+    ri = np.repeat(rows, N2).astype(np.int64)
+    ni = np.tile(np.arange(N2, dtype=np.int64), rows.size)
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < 1.0:
+        t0 = time.perf_counter()
+        gu = oracle.grouped_contiguous_at(w.A, w.B, w.sfA, w.sfB, w.m_indices, ri, ni)
+        h = oracle.swiglu(gu.reshape(rows.size, N2))
+        rc, rs = oracle.quantize_blocks(h.astype(np.float32), 1, 128)
+        dt += time.perf_counter() - t0
+        reps += 1
+    dt /= reps
+    st = g.sets[last_set % len(g.sets)]
+    codes = st["codes"].view(torch.uint8).cpu().numpy()[rows]
+    sf = st["sf"].cpu().numpy()[rows]
+    check = dict(n=int(rc.size), code_match=float((codes == rc).mean()),
+                 scale_match=float((sf == rs).mean()))
+    sample = f"{g.name}: {rows.size} of {n_rows} rows x {N2} gate/up columns, {dt:.3f} s (mean of {reps})"
+    return dt * n_rows / rows.size, sample, {g.name: check}
 
 
 class Quant:
@@ -300,7 +368,9 @@ def main():
         if args.gemm not in names:
             sys.exit(f"--gemm {args.gemm} is not part of workload {args.workload}: {names}")
         names = [args.gemm]
-    gemms = [Quant(n, *QUANT_SHAPES[n]) if n in QUANT_SHAPES else Gemm(n, synth.workload(n), args.sfa)
+    gemms = [Quant(n, *QUANT_SHAPES[n]) if n in QUANT_SHAPES else
+             SwigluGemm(n, synth.workload("moe_cont")) if n == "moe_cont_swiglu" else
+             Gemm(n, synth.workload(n), args.sfa)
              for n in names]
     step_footprint = sum(g.footprint for g in gemms)
     copies = max(1, -(-ROTATE_BYTES // step_footprint))
@@ -378,6 +448,8 @@ def main():
     if not args.no_cpu_baseline:
         if args.workload == "quant":
             per_step, sample, checks = quant_oracle_leg(gemms[0], args.warmup + K - 1)
+        elif args.workload == "moe_swiglu":
+            per_step, sample, checks = swiglu_oracle_leg(gemms[0], args.warmup + K - 1)
         else:
             per_step, sample, checks = oracle_leg(gemms, args.warmup + K - 1, args.sfa)
         import oracle
@@ -407,7 +479,10 @@ def main():
                    {"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) quantized to "
                     "e4m3fn, A per 1x128, B per 128x128, power-of-two scales",
                     "sfa_layout": "packed UE8M0" if args.sfa == "ue8m0" else "fp32",
-                    "accumulate": "fp32", "output": "bf16", "parallelism": "single GPU",
+                    "accumulate": "fp32",
+                    "output": ("e4m3fn codes + fp32 scale per 1x128 of silu(gate) * up"
+                               if args.workload == "moe_swiglu" else "bf16"),
+                    "parallelism": "single GPU",
                     "rotation_copies": copies}),
         "roofline": roof,
         "cpu_baseline": cpu,
