@@ -18,6 +18,8 @@ and the passages of the pages it follows, are stated in that file:
 * ``quantize_blocks``: power-of-two per-block scale and nearest-e4m3fn codes, written
   as a search (launch article section 1.2).
 * ``bf16_rne``: one rounding from fp64 to bf16.
+* ``gemm``: the dense product in the NT / NN / TN / TT memory layouts -- project
+  page, "core features".
 * ``swiglu``: h = silu(gate) * up between the two grouped GEMMs of an MoE layer --
   project page, "core features" (Mega MoE: Linear1, SwiGLU, Linear2 fused).
 * ``unpack_ue8m0``: fp32 scales from the packed exponent-byte (UE8M0) layout of the
@@ -83,6 +85,8 @@ def _load():
     lib.dgo_e4m3fn_nearest.restype = ctypes.c_uint8
     lib.dgo_e4m3fn_nearest.argtypes = [ctypes.c_double]
     lib.dgo_quantize_blocks.argtypes = [_f32p, _i64, _i64, _i64, _i64, _u8p, _f32p]
+    lib.dgo_gemm_layout.argtypes = [_u8p, _u8p, _f32p, _f32p, _i64, _i64, _i64, ctypes.c_int,
+                                    ctypes.c_int, _f64p]
     lib.dgo_swiglu.argtypes = [_f64p, _i64, _i64, _f64p]
     lib.dgo_unpack_ue8m0.argtypes = [ctypes.POINTER(ctypes.c_uint32), _i64, _i64, _f32p]
     lib.dgo_num_threads.restype = ctypes.c_int
@@ -220,6 +224,24 @@ def scale_exponent(amax: float) -> int:
 
 def e4m3fn_nearest(y: float) -> int:
     return int(_load().dgo_e4m3fn_nearest(float(y)))
+
+
+def gemm(A, B, sfA, sfB, layout: str = "nt") -> np.ndarray:
+    """C_exact [M][N] of C = op(A) op(B), layout "nt" | "nn" | "tn" | "tt": A stored
+    [M][K] (first letter n) or [K][M] (t); B stored [K][N] (second letter n) or [N][K] (t)."""
+    assert layout in ("nt", "nn", "tn", "tt")
+    a_t, b_n = layout[0] == "t", layout[1] == "n"
+    A, B = _codes(A), _codes(B)
+    sfA = np.ascontiguousarray(sfA, dtype=np.float32)
+    sfB = np.ascontiguousarray(sfB, dtype=np.float32)
+    M = A.shape[1] if a_t else A.shape[0]
+    K = A.shape[0] if a_t else A.shape[1]
+    N = B.shape[1] if b_n else B.shape[0]
+    assert (B.shape[0] if b_n else B.shape[1]) == K
+    C = np.empty((M, N), dtype=np.float64)
+    _load().dgo_gemm_layout(_p(A, _u8p), _p(B, _u8p), _p(sfA, _f32p), _p(sfB, _f32p), M, N, K,
+                            int(a_t), int(b_n), _p(C, _f64p))
+    return C
 
 
 def swiglu(gu) -> np.ndarray:

@@ -134,6 +134,36 @@ void dgo_gemm_nt(const uint8_t* A, const uint8_t* B, const float* sfA, const flo
   }
 }
 
+/* Dense GEMM in the other memory layouts (DeepGEMM project page, aiproducthub.cn,
+ * "core features": NT/TN/NN/TT layouts of one GEMM family). C = op(A) op(B) with the
+ * same block scaling: a(m, k) is A[m][k] (A stored [M][K]) or, with a_t, A[k][m] (A
+ * stored [K][M]); b(n, k) is B[n][k] (B stored [N][K]) or, with b_n, B[k][n] (B stored
+ * [K][N]). sfA [M][K/128] and sfB [ceil(N/128)][K/128] as for NT. Written with the
+ * strided indexing spelled out; every block sum is exact as in dgo_scaled_dot. */
+void dgo_gemm_layout(const uint8_t* A, const uint8_t* B, const float* sfA, const float* sfB,
+                     int64_t M, int64_t N, int64_t K, int a_t, int b_n, double* C_exact) {
+  double val[256];
+  int64_t KB = K / DGO_KBLOCK, m;
+  dgo_value_table(val);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (m = 0; m < M; ++m) {
+    int64_t n, kb, k;
+    for (n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (kb = 0; kb < KB; ++kb) {
+        double block = 0.0;
+        for (k = kb * DGO_KBLOCK; k < (kb + 1) * DGO_KBLOCK; ++k) {
+          uint8_t a = a_t ? A[k * M + m] : A[m * K + k];
+          uint8_t b = b_n ? B[k * N + n] : B[n * K + k];
+          block += val[a] * val[b];
+        }
+        acc += block * (double)sfA[m * KB + kb] * (double)sfB[(n / DGO_KBLOCK) * KB + kb];
+      }
+      C_exact[m * N + n] = acc;
+    }
+  }
+}
+
 /* Dense NT at chosen output positions (m_idx[i], n_idx[i]), i < count. */
 void dgo_gemm_nt_at(const uint8_t* A, const uint8_t* B, const float* sfA, const float* sfB,
                     int64_t M, int64_t N, int64_t K, const int64_t* m_idx,

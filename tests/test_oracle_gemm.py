@@ -247,3 +247,22 @@ def test_grouped_hand_example_rows():
     assert np.array_equal(C[0], np.array(d["C"][0]))
     Cm, pm = oracle.grouped_masked(A[None], B, sfA[None], sfB, np.array([2], dtype=np.int32))
     assert np.array_equal(Cm[0], np.array(d["C"]))
+
+
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (3, 17, 256), (4, 130, 128)])
+def test_layouts_exact_rational(layout, M, N, K):
+    # op(A) op(B) with A stored [K][M] for "t" and B stored [K][N] for "n": against the
+    # exact-rational NT product of transposed copies
+    rng = np.random.default_rng(M * 7 + N + K + ord(layout[0]) + 3 * ord(layout[1]))
+    A_mk, B_nk = rand_codes(rng, (M, K)), rand_codes(rng, (N, K))
+    sfA = pow2_scales(rng, (M, K // 128))
+    sfB = pow2_scales(rng, ((N + 127) // 128, K // 128))
+    A = np.ascontiguousarray(A_mk.T) if layout[0] == "t" else A_mk
+    B = np.ascontiguousarray(B_nk.T) if layout[1] == "n" else B_nk
+    C = oracle.gemm(A, B, sfA, sfB, layout)
+    ex = _exact.exact_gemm(A_mk, B_nk, sfA, sfB)
+    for m in range(M):
+        for n in range(N):
+            assert Fraction(float(C[m, n])) == ex[m][n]
+    assert np.array_equal(C, oracle.gemm_nt(A_mk, B_nk, sfA, sfB))
