@@ -8,7 +8,7 @@ fallback path. If libdg.so is missing the import fails.
 Calls (DeepGEMM project page, aiproducthub.cn, "quick start"; DeepGEMM launch
 article, deepseek.csdn.net, section 4.2 "advanced tuning"):
 
-* ``fp8_gemm_nt(a, b, c, a_sf, b_sf)``
+* ``fp8_gemm_nt(a, b, c, a_sf, b_sf)`` and ``fp8_gemm_nn / _tn / _tt`` (other layouts)
 * ``m_grouped_fp8_gemm_nt_contiguous(a, b, c, a_sf, b_sf, m_indices)``
 * ``m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None)``
 * ``quantize_fp8_1x128(x, codes=None, sf=None)``: activations -> (A codes, sfA)
@@ -68,6 +68,9 @@ lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu.argtypes = [_vp, _vp, _vp, _vp, _
 lib.dg_m_grouped_fp8_gemm_nt_masked_swiglu.restype = ctypes.c_int
 lib.dg_m_grouped_fp8_gemm_nt_masked_swiglu.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                       _i64, _i64, _i64, _vp]
+for _name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
+    getattr(lib, _name).restype = ctypes.c_int
+    getattr(lib, _name).argtypes = lib.dg_fp8_gemm_nt.argtypes
 lib.dg_quantize_fp8_1x128.restype = ctypes.c_int
 lib.dg_quantize_fp8_1x128.argtypes = [_vp, _i32, _vp, _vp, _i64, _i64, _vp]
 
@@ -150,6 +153,39 @@ def fp8_gemm_nt(a, b, c, a_sf, b_sf) -> None:
     with torch.cuda.device(dev):
         check(fn(a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
                  M, N, K, _stream(dev)))
+
+
+def _fp8_gemm_layout(layout: str, a, b, c, a_sf, b_sf) -> None:
+    _fp8(a, "a"), _fp8(b, "b")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    M, K = (a.shape[1], a.shape[0]) if layout[0] == "t" else tuple(a.shape)
+    N = b.shape[1] if layout[1] == "n" else b.shape[0]
+    dev = a.device
+    _dev(a, "a", dev)
+    _need(b, "b", b.dtype, (K, N) if layout[1] == "n" else (N, K), dev)
+    _need(c, "c", torch.bfloat16, (M, N), dev)
+    _need(a_sf, "a_sf", torch.float32, (M, K // BLOCK), dev)
+    _need(b_sf, "b_sf", torch.float32, ((N + BLOCK - 1) // BLOCK, K // BLOCK), dev)
+    fn = getattr(lib, "dg_fp8_gemm_" + layout)
+    with torch.cuda.device(dev):
+        check(fn(a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
+                 M, N, K, _stream(dev)))
+
+
+def fp8_gemm_nn(a, b, c, a_sf, b_sf) -> None:
+    """c [M][N] = a [M][K] x b [K][N] (block-scaled; scales as for fp8_gemm_nt)."""
+    _fp8_gemm_layout("nn", a, b, c, a_sf, b_sf)
+
+
+def fp8_gemm_tn(a, b, c, a_sf, b_sf) -> None:
+    """c [M][N] = a [K][M]^T x b [K][N]."""
+    _fp8_gemm_layout("tn", a, b, c, a_sf, b_sf)
+
+
+def fp8_gemm_tt(a, b, c, a_sf, b_sf) -> None:
+    """c [M][N] = a [K][M]^T x b [N][K]^T."""
+    _fp8_gemm_layout("tt", a, b, c, a_sf, b_sf)
 
 
 def m_grouped_fp8_gemm_nt_contiguous(a, b, c, a_sf, b_sf, m_indices) -> None:
@@ -296,6 +332,6 @@ def config_names() -> list[str]:
     return [lib.dg_config_name(i).decode() for i in range(lib.dg_num_configs())]
 
 
-__all__ = ["config_names", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+__all__ = ["config_names", "fp8_gemm_nt", "fp8_gemm_nn", "fp8_gemm_tn", "fp8_gemm_tt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
            "m_grouped_fp8_gemm_nt_contiguous_swiglu", "m_grouped_fp8_gemm_nt_masked_swiglu",
            "quantize_fp8_1x128", "describe_config", "DGError", "lib", "LIB_PATH"]

@@ -25,6 +25,7 @@
 #include "quant_kernel.hpp"
 #include "skinny_kernel.hpp"
 #include "stream_kernel.hpp"
+#include "transpose_kernel.hpp"
 
 namespace dg {
 namespace {
@@ -164,7 +165,14 @@ struct Workspace {
   size_t partial_bytes = 0;
   uint32_t* counters = nullptr;
   size_t counter_count = 0;
+  void* a_t = nullptr;  // K-contiguous copies of operands given in another layout
+  size_t a_t_bytes = 0;
+  void* b_t = nullptr;
+  size_t b_t_bytes = 0;
 };
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 dg_status grow(void** buf, size_t* have, size_t need, size_t elem, hipStream_t stream, bool zero) {
   if (*have >= need) return DG_OK;
@@ -184,13 +192,11 @@ dg_status grow(void** buf, size_t* have, size_t need, size_t elem, hipStream_t s
 
 dg_status get_workspace(hipStream_t stream, size_t partial_bytes, size_t counters,
                         float** partials, uint32_t** counter_ptr) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, Workspace> table;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(DG_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
-  std::lock_guard<std::mutex> lock(mu);
-  Workspace& w = table[std::make_pair(dev, stream)];
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[std::make_pair(dev, stream)];
   dg_status st = grow(&w.partials, &w.partial_bytes, partial_bytes, 1, stream, false);
   if (st != DG_OK) return st;
   st = grow((void**)&w.counters, &w.counter_count, counters, sizeof(uint32_t), stream, true);
@@ -198,6 +204,34 @@ dg_status get_workspace(hipStream_t stream, size_t partial_bytes, size_t counter
   *partials = (float*)w.partials;
   *counter_ptr = w.counters;
   return DG_OK;
+}
+
+// The per-(device, stream) buffers for K-contiguous copies of A (a_bytes) and B.
+dg_status get_transpose_workspace(hipStream_t stream, size_t a_bytes, size_t b_bytes,
+                                  uint8_t** a, uint8_t** b) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DG_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[std::make_pair(dev, stream)];
+  dg_status st = grow(&w.a_t, &w.a_t_bytes, a_bytes, 1, stream, false);
+  if (st != DG_OK) return st;
+  st = grow(&w.b_t, &w.b_t_bytes, b_bytes, 1, stream, false);
+  if (st != DG_OK) return st;
+  *a = (uint8_t*)w.a_t;
+  *b = (uint8_t*)w.b_t;
+  return DG_OK;
+}
+
+// dst [C][R] = src [R][C]^T (bytes), R a multiple of 128.
+dg_status launch_transpose(const uint8_t* src, uint8_t* dst, int64_t R, int64_t C,
+                           hipStream_t stream) {
+  const int64_t tiles_c = (C + kTrTile - 1) / kTrTile, tiles = (R / kTrTile) * tiles_c;
+  if (tiles > 0x7FFFFFFF) return fail(DG_ERR_UNSUPPORTED_SHAPE, "transpose of %lld tiles", (long long)tiles);
+  hipLaunchKernelGGL(transpose_bytes_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, src, dst,
+                     R, C, tiles_c);
+  const hipError_t err = hipGetLastError();
+  return err == hipSuccess ? DG_OK : fail(DG_ERR_LAUNCH, "transpose: %s", hipGetErrorString(err));
 }
 
 template <class Cfg>
@@ -682,6 +716,51 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_swiglu(const void* A, const void* B, v
   p.K = K;
   p.G = G;
   return launch_pipe_swiglu<kMasked>(p, G, I, (uint8_t*)codes, sf, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace dg {
+namespace {
+
+// C = op(A) op(B): operands not stored K-contiguous (A as [K][M], B as [K][N]) are
+// first transposed into the stream's workspace, then the NT kernels run on them.
+dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
+                      const float* sfB, int64_t M, int64_t N, int64_t K, bool a_t, bool b_n,
+                      void* stream) {
+  g_detail[0] = 0;
+  if (M < 0) return fail(DG_ERR_BAD_SHAPE, "negative M=%lld", (long long)M);
+  dg_status s = check_common(A, B, C, sfA, sfB, N, K, M > 0 && N > 0);
+  if (s != DG_OK || M == 0 || N == 0) return s;
+  if (M > (int64_t)1 << 30) return fail(DG_ERR_UNSUPPORTED_SHAPE, "M beyond 2^30");
+  const hipStream_t st = (hipStream_t)stream;
+  uint8_t *a2 = nullptr, *b2 = nullptr;
+  s = get_transpose_workspace(st, a_t ? (size_t)(M * K) : 0, b_n ? (size_t)(N * K) : 0, &a2, &b2);
+  if (s != DG_OK) return s;
+  if (a_t && (s = launch_transpose((const uint8_t*)A, a2, K, M, st)) != DG_OK) return s;
+  if (b_n && (s = launch_transpose((const uint8_t*)B, b2, K, N, st)) != DG_OK) return s;
+  return gemm_dense(a_t ? (const void*)a2 : A, b_n ? (const void*)b2 : B, C, sfA, 0, sfB, M, N, K,
+                    stream);
+}
+
+}  // namespace
+}  // namespace dg
+
+extern "C" {
+
+dg_status dg_fp8_gemm_nn(const void* A, const void* B, void* C, const float* sfA,
+                         const float* sfB, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_layout(A, B, C, sfA, sfB, M, N, K, false, true, stream);
+}
+
+dg_status dg_fp8_gemm_tn(const void* A, const void* B, void* C, const float* sfA,
+                         const float* sfB, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_layout(A, B, C, sfA, sfB, M, N, K, true, true, stream);
+}
+
+dg_status dg_fp8_gemm_tt(const void* A, const void* B, void* C, const float* sfA,
+                         const float* sfB, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_layout(A, B, C, sfA, sfB, M, N, K, true, false, stream);
 }
 
 dg_status dg_quantize_fp8_1x128(const void* x, int32_t x_dtype, void* codes, float* sf,

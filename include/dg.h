@@ -72,6 +72,28 @@ dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA
                          void* hip_stream);
 
 /*
+ * The same dense GEMM in the other memory layouts of one GEMM family (project page,
+ * "core features": NT / TN / NN / TT layouts, for forward, backward and inference):
+ * C = op(A) op(B) with op = N (as stored) or T (transposed), i.e.
+ *   dg_fp8_gemm_nn:  A e4m3fn [M][K],  B e4m3fn [K][N]
+ *   dg_fp8_gemm_tn:  A e4m3fn [K][M],  B e4m3fn [K][N]
+ *   dg_fp8_gemm_tt:  A e4m3fn [K][M],  B e4m3fn [N][K]
+ * (dg_fp8_gemm_nt above is A [M][K], B [N][K]). The scales keep their meaning and
+ * layout: sfA fp32 [M][K/128] (row m, K-block kb), sfB fp32 [ceil(N/128)][K/128]; C is
+ * bf16 [M][N]. Same shape, alignment and error rules as dg_fp8_gemm_nt. An operand
+ * that is not K-contiguous is first transposed into a library-owned buffer of the
+ * stream (M*K or N*K bytes, kept and reused by later calls on that stream, released
+ * only when the process ends); the results equal dg_fp8_gemm_nt's on the transposed
+ * operands bit for bit.
+ */
+dg_status dg_fp8_gemm_nn(const void* A, const void* B, void* C, const float* sfA,
+                         const float* sfB, int64_t M, int64_t N, int64_t K, void* hip_stream);
+dg_status dg_fp8_gemm_tn(const void* A, const void* B, void* C, const float* sfA,
+                         const float* sfB, int64_t M, int64_t N, int64_t K, void* hip_stream);
+dg_status dg_fp8_gemm_tt(const void* A, const void* B, void* C, const float* sfA,
+                         const float* sfB, int64_t M, int64_t N, int64_t K, void* hip_stream);
+
+/*
  * MoE grouped GEMM, contiguous layout (project page, "technical implementation":
  * several experts' token rows concatenated along M, N and K shared).
  *   A   e4m3fn [M_total][K]      sfA fp32 [M_total][K/128]
