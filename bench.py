@@ -79,9 +79,10 @@ def kernel_source_hash() -> str:
 class Gemm:
     """One GEMM of the workload: host inputs, device copies, algorithmic work."""
 
-    def __init__(self, name, w, sfa_layout: str = "f32"):
+    def __init__(self, name, w, sfa_layout: str = "f32", layout: str = "nt"):
         import numpy as np
         self.name, self.w = name, w
+        self.layout = layout
         self.kind = type(w).__name__.lower()
         if self.kind == "dense":
             M, N, K = w.shape
@@ -106,6 +107,7 @@ class Gemm:
                           + (M * N * 2 if self.kind != "masked" else G * M * N * 2))
 
     def upload(self, copies: int, sfa_layout: str = "f32"):
+        import numpy as np
         import torch
         import synth
         dev = torch.device("cuda:0")
@@ -114,7 +116,12 @@ class Gemm:
             return torch.from_numpy(x).to(dev)
 
         sfa = synth.pack_ue8m0(self.w.sfA) if sfa_layout == "ue8m0" else self.w.sfA
-        base = dict(A=t(self.w.A).view(torch.float8_e4m3fn), B=t(self.w.B).view(torch.float8_e4m3fn),
+        a_host, b_host = self.w.A, self.w.B
+        if self.kind == "dense" and self.layout[0] == "t":
+            a_host = np.ascontiguousarray(a_host.T)  # A stored [K][M]
+        if self.kind == "dense" and self.layout[1] == "n":
+            b_host = np.ascontiguousarray(b_host.T)  # B stored [K][N]
+        base = dict(A=t(a_host).view(torch.float8_e4m3fn), B=t(b_host).view(torch.float8_e4m3fn),
                     sfA=t(sfa), sfB=t(self.w.sfB))
         if self.kind == "contiguous":
             base["idx"] = t(self.w.m_indices)
@@ -134,7 +141,7 @@ class Gemm:
         import fp8_block_scaled_dg_amd as dg
         s = self.sets[i % len(self.sets)]
         if self.kind == "dense":
-            dg.fp8_gemm_nt(s["A"], s["B"], s["C"], s["sfA"], s["sfB"])
+            getattr(dg, "fp8_gemm_" + self.layout)(s["A"], s["B"], s["C"], s["sfA"], s["sfB"])
         elif self.kind == "contiguous":
             dg.m_grouped_fp8_gemm_nt_contiguous(s["A"], s["B"], s["C"], s["sfA"], s["sfB"],
                                                 s["idx"])
@@ -333,6 +340,9 @@ def main():
                          "time has passed, so that the GPU clocks have left their idle state")
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=("nt", "nn", "tn", "tt"), default="nt",
+                    help="memory layout of the dense GEMMs' operands (A [K][M] for t, "
+                         "B [K][N] for n); the timed call includes the transposition")
     ap.add_argument("--sfa", choices=("f32", "ue8m0"), default="f32",
                     help="layout of the A scales: fp32 values, or packed UE8M0 exponent bytes")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -370,7 +380,7 @@ def main():
         names = [args.gemm]
     gemms = [Quant(n, *QUANT_SHAPES[n]) if n in QUANT_SHAPES else
              SwigluGemm(n, synth.workload("moe_cont")) if n == "moe_cont_swiglu" else
-             Gemm(n, synth.workload(n), args.sfa)
+             Gemm(n, synth.workload(n), args.sfa, args.layout)
              for n in names]
     step_footprint = sum(g.footprint for g in gemms)
     copies = max(1, -(-ROTATE_BYTES // step_footprint))
@@ -479,6 +489,7 @@ def main():
                    {"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) quantized to "
                     "e4m3fn, A per 1x128, B per 128x128, power-of-two scales",
                     "sfa_layout": "packed UE8M0" if args.sfa == "ue8m0" else "fp32",
+                    "operand_layout": args.layout.upper(),
                     "accumulate": "fp32",
                     "output": ("e4m3fn codes + fp32 scale per 1x128 of silu(gate) * up"
                                if args.workload == "moe_swiglu" else "bf16"),
