@@ -117,7 +117,9 @@ dg_status launch_pipe(const Problem& p0, int64_t blocks, hipStream_t stream) {
       grid = ts.full + split * ts.parts;
     }
   }
-  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream, a);
+  a.items = (int32_t)grid;
+  const int64_t wgs = grid < kCUs ? grid : kCUs;  // persistent, one workgroup per CU
+  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND>), dim3((unsigned)wgs), dim3(Cfg::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
   return DG_OK;
@@ -144,7 +146,9 @@ dg_status launch_pipe_swiglu(const Problem& p0, int64_t blocks, int64_t I, uint8
   a.sw.codes = codes;
   a.sw.sf = sf;
   a.sw.I = (int32_t)I;
-  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND, true>), dim3((unsigned)grid), dim3(Cfg::NT), 0, stream,
+  a.items = (int32_t)grid;
+  const int64_t wgs = grid < kCUs ? grid : kCUs;  // persistent, one workgroup per CU
+  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND, true>), dim3((unsigned)wgs), dim3(Cfg::NT), 0, stream,
                      a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));

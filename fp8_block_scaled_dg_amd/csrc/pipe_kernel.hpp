@@ -468,36 +468,57 @@ __device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& 
 
 // bf16 RNE store of a finished tile: produced rows (< valid_rows, and for the
 // contiguous layout only rows whose m_indices entry equals `expert`) and in-range
-// columns only.
+// columns only. A lane of the MFMA result holds 4 columns of one row, so storing
+// from registers would put 16 bytes into each of 32 rows per instruction, and the
+// L2 would take every one as a partial-line write. Instead each wave passes its
+// 64x64 sub-tile through its own 4 KB of LDS stage 2, 32 rows at a time, and reads
+// it back with 8 lanes per row: each store instruction then writes 8 whole 128-byte
+// row segments, an eighth of the write requests. Stage 2 is refilled only after the
+// barrier that follows the next tile's first DMAs, which a wave reaches after its
+// store. 16-byte chunk q of staged row r sits at chunk q ^ (r & 7), which spreads
+// both the writes (8-byte halves of one chunk column from 32 rows) and the reads
+// (a whole row per 8 lanes) evenly over the banks.
 template <class Cfg, int KIND>
 __device__ __forceinline__ void pipe_store(const Problem& p, const TileView& v, int expert,
                                            int valid_rows, const v16f (&acc)[Cfg::TM][Cfg::TN]) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(TN == 2 && Cfg::NW * 4096 <= kPipeStageBytes, "64-column sub-tiles, 4 KB per wave");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t N = p.N;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int r32 = lane & 31, g = lane >> 5;
+  uint8_t* lds = pipe_stage2 + wave * 4096;
+  const int rr = lane >> 3, ch = lane & 7;  // read side: rows rr + 8k, chunk ch
+  const int64_t col = v.n0 + wn * 64 + 8 * ch;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t row = v.m0 + wm * 64 + i * 32 + r32;
-    bool ok = row < (int64_t)valid_rows;
-    if (KIND == kContiguous && ok) ok = p.m_indices[row] == expert;
-    if (!ok) continue;
-    uint16_t* crow = v.C + row * N;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int64_t col = v.n0 + wn * 64 + j * 32 + 8 * e4 + 4 * g;
-        if (col < N) {
-          const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 0]) |
-                              ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 1]) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 2]) |
-                              ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 3]) << 16);
-          *(uint2*)(crow + col) = make_uint2(lo, hi);
-        }
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 0]) |
+                            ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 2]) |
+                            ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * e4 + 3]) << 16);
+        *(uint2*)(lds + r32 * 128 + (((4 * j + e4) ^ (r32 & 7)) << 4) + 8 * g) =
+            make_uint2(lo, hi);
       }
+    // the wave's LDS accesses run in order; this keeps the compiler from moving
+    // the reads of other lanes' data above the writes (and the next writes above
+    // these reads)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    wait_vm_lgkm0<63>();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 8 * k + rr;
+      const v4u d = *(const v4u*)(lds + r * 128 + ((ch ^ rr) << 4));
+      const int64_t row = v.m0 + wm * 64 + i * 32 + r;
+      bool ok = row < (int64_t)valid_rows && col < N;
+      if (KIND == kContiguous && ok) ok = p.m_indices[row] == expert;
+      if (ok) *(v4u*)(v.C + row * N + col) = d;
     }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   }
 }
 
@@ -679,6 +700,7 @@ struct PipeArgs {
   uint32_t* counters;  // split tail: one per tile, zero between calls
   int32_t full_tiles;  // dense: tiles computed whole (the first of the tile order)
   int32_t parts;       // dense: K parts of each remaining tile
+  int32_t items;       // work items: dense full tiles + split parts, or the grid's tiles
   SwigluOut sw;        // fused SwiGLU epilogue (grouped layouts): outputs and I
 };
 
@@ -756,16 +778,18 @@ __device__ __forceinline__ void pipe_split_tile(const PipeArgs& a, const TileVie
   pipe_store<Cfg, kDense>(a.p, v, 0, (int)a.p.M, sum);
 }
 
+// One work item: a tile (or, dense, a K part of a tail tile). `item` plays the role
+// of the workgroup index in the tile order: item i runs on XCD i % 8.
 // SWIGLU (grouped layouts, 128x256 tiles): B is [gate; up] with 2 * sw.I rows per
 // expert, tile tn covers gate columns 128 tn.. and the matching up columns, and the
 // fused epilogue writes quantized h instead of bf16 C.
-template <class Cfg, int KIND, bool SWIGLU = false>
-__global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
+template <class Cfg, int KIND, bool SWIGLU>
+__device__ __forceinline__ void pipe_item(const PipeArgs& args, int item) {
   static_assert(!SWIGLU || KIND != kDense, "the fused epilogue is for the grouped layouts");
   constexpr int NSTEP = SWIGLU ? 128 : Cfg::BN;  // columns between consecutive N-tiles
   const Problem& p = args.p;
-  if (KIND == kDense && (int)blockIdx.x >= args.full_tiles) {
-    const int h = (int)blockIdx.x - args.full_tiles;
+  if (KIND == kDense && item >= args.full_tiles) {
+    const int h = item - args.full_tiles;
     const int tt = h / args.parts, part = h - tt * args.parts;
     int tm, tn;
     grouped_tile<Cfg::GROUP_M>(args.full_tiles + tt, p.tiles_m, p.tiles_n, tm, tn);
@@ -789,7 +813,7 @@ __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
   if (KIND == kMasked) {
     // only the live tiles are dealt out: the grid covers every expert at full
     // height, the workgroups past the live count leave at once
-    const MaskedTile mt = masked_tile<Cfg::BM>(p.masked_m, p.G, (int)p.M, p.tiles_n, blockIdx.x);
+    const MaskedTile mt = masked_tile<Cfg::BM>(p.masked_m, p.G, (int)p.M, p.tiles_n, item);
     if (mt.expert < 0) return;
     const int e = mt.expert, valid = mt.valid;
     grouped_tile<Cfg::GROUP_M>(mt.local, (valid + Cfg::BM - 1) / Cfg::BM, p.tiles_n, tm, tn);
@@ -807,7 +831,7 @@ __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
     pipe_tile<Cfg, KIND, SWIGLU>(p, v, e, valid, true, sw);
     return;
   }
-  const int t = xcd_tile_order(blockIdx.x, KIND == kDense ? args.full_tiles : gridDim.x);
+  const int t = xcd_tile_order(item, KIND == kDense ? args.full_tiles : args.items);
   grouped_tile<Cfg::GROUP_M>(t, p.tiles_m, p.tiles_n, tm, tn);
   v.m0 = (int64_t)tm * Cfg::BM;
   v.n0 = (int64_t)tn * NSTEP;
@@ -850,6 +874,16 @@ __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
     pipe_tile<Cfg, KIND, SWIGLU>(p, v, e, (int)p.M, any_row, args.sw);
     prev = e;
   }
+}
+
+// Persistent: at most one workgroup per CU, each taking items blockIdx.x,
+// blockIdx.x + gridDim.x, ... (gridDim.x is the item count, or a multiple of 8 when
+// smaller, so item i stays on XCD i % 8). A tile's stores drain while the next
+// tile's first DMAs are in flight, and no workgroup is dispatched per tile.
+template <class Cfg, int KIND, bool SWIGLU = false>
+__global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
+  for (int item = blockIdx.x; item < args.items; item += gridDim.x)
+    pipe_item<Cfg, KIND, SWIGLU>(args, item);
 }
 
 }  // namespace dg
