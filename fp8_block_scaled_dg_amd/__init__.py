@@ -104,11 +104,13 @@ def _fp8(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device) -> None:
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    _dev(t, name, device)
+    # one combined test on the common path; the specific error only on failure
+    if t.dtype != dtype or t.shape != shape or t.device != device or not t.is_contiguous():
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        _dev(t, name, device)
 
 
 def _dev(t: torch.Tensor, name: str, device) -> None:
@@ -120,8 +122,23 @@ def _dev(t: torch.Tensor, name: str, device) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def _stream(device) -> int:
-    return torch.cuda.current_stream(device).cuda_stream
+_current_device = torch.cuda.current_device
+_raw_stream = torch._C._cuda_getCurrentRawStream
+
+
+def _run(dev, fn, *args) -> None:
+    """fn(*args, stream): the library call on torch's current stream of `dev`, with
+    `dev` the current device (the library keeps its workspace per device and stream).
+    The device is switched only when it is not current already. Raises DGError on a
+    nonzero status."""
+    idx = dev.index
+    if _current_device() == idx:
+        status = fn(*args, _raw_stream(idx))
+    else:
+        with torch.cuda.device(idx):
+            status = fn(*args, _raw_stream(idx))
+    if status:
+        raise DGError(status)
 
 
 def _a_sf_layout(a_sf, lead: tuple, K: int, dev):
@@ -150,9 +167,8 @@ def fp8_gemm_nt(a, b, c, a_sf, b_sf) -> None:
     packed = _a_sf_layout(a_sf, (M,), K, dev)
     _need(b_sf, "b_sf", torch.float32, ((N + BLOCK - 1) // BLOCK, K // BLOCK), dev)
     fn = lib.dg_fp8_gemm_nt_ue8m0 if packed else lib.dg_fp8_gemm_nt
-    with torch.cuda.device(dev):
-        check(fn(a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
-                 M, N, K, _stream(dev)))
+    _run(dev, fn, a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
+         M, N, K)
 
 
 def _fp8_gemm_layout(layout: str, a, b, c, a_sf, b_sf) -> None:
@@ -168,9 +184,8 @@ def _fp8_gemm_layout(layout: str, a, b, c, a_sf, b_sf) -> None:
     _need(a_sf, "a_sf", torch.float32, (M, K // BLOCK), dev)
     _need(b_sf, "b_sf", torch.float32, ((N + BLOCK - 1) // BLOCK, K // BLOCK), dev)
     fn = getattr(lib, "dg_fp8_gemm_" + layout)
-    with torch.cuda.device(dev):
-        check(fn(a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
-                 M, N, K, _stream(dev)))
+    _run(dev, fn, a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
+         M, N, K)
 
 
 def fp8_gemm_nn(a, b, c, a_sf, b_sf) -> None:
@@ -205,10 +220,8 @@ def m_grouped_fp8_gemm_nt_contiguous(a, b, c, a_sf, b_sf, m_indices) -> None:
     _need(m_indices, "m_indices", torch.int32, (M,), dev)
     fn = (lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 if packed
           else lib.dg_m_grouped_fp8_gemm_nt_contiguous)
-    with torch.cuda.device(dev):
-        check(fn(
-            a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
-            m_indices.data_ptr(), M, N, K, G, _stream(dev)))
+    _run(dev, fn, a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
+         m_indices.data_ptr(), M, N, K, G)
 
 
 def m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None) -> None:
@@ -228,10 +241,8 @@ def m_grouped_fp8_gemm_nt_masked(a, b, c, a_sf, b_sf, masked_m, expected_m=None)
     _need(masked_m, "masked_m", torch.int32, (G,), dev)
     em = int(expected_m) if expected_m is not None else 0
     fn = lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0 if packed else lib.dg_m_grouped_fp8_gemm_nt_masked
-    with torch.cuda.device(dev):
-        check(fn(
-            a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
-            masked_m.data_ptr(), G, M_max, N, K, em, _stream(dev)))
+    _run(dev, fn, a.data_ptr(), b.data_ptr(), c.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(),
+         masked_m.data_ptr(), G, M_max, N, K, em)
 
 
 def _swiglu_outputs(lead: tuple, I: int, codes, sf, dev):
@@ -263,10 +274,9 @@ def m_grouped_fp8_gemm_nt_contiguous_swiglu(a, b, a_sf, b_sf, m_indices, codes=N
     _need(b_sf, "b_sf", torch.float32, (G, N2 // BLOCK, K // BLOCK), dev)
     _need(m_indices, "m_indices", torch.int32, (M,), dev)
     codes, sf = _swiglu_outputs((M,), I, codes, sf, dev)
-    with torch.cuda.device(dev):
-        check(lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu(
-            a.data_ptr(), b.data_ptr(), codes.data_ptr(), sf.data_ptr(), a_sf.data_ptr(),
-            b_sf.data_ptr(), m_indices.data_ptr(), M, I, K, G, _stream(dev)))
+    _run(dev, lib.dg_m_grouped_fp8_gemm_nt_contiguous_swiglu, a.data_ptr(), b.data_ptr(),
+         codes.data_ptr(), sf.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(), m_indices.data_ptr(),
+         M, I, K, G)
     return codes, sf
 
 
@@ -287,10 +297,9 @@ def m_grouped_fp8_gemm_nt_masked_swiglu(a, b, a_sf, b_sf, masked_m, codes=None, 
     _need(b_sf, "b_sf", torch.float32, (G, N2 // BLOCK, K // BLOCK), dev)
     _need(masked_m, "masked_m", torch.int32, (G,), dev)
     codes, sf = _swiglu_outputs((G, M_max), I, codes, sf, dev)
-    with torch.cuda.device(dev):
-        check(lib.dg_m_grouped_fp8_gemm_nt_masked_swiglu(
-            a.data_ptr(), b.data_ptr(), codes.data_ptr(), sf.data_ptr(), a_sf.data_ptr(),
-            b_sf.data_ptr(), masked_m.data_ptr(), G, M_max, I, K, _stream(dev)))
+    _run(dev, lib.dg_m_grouped_fp8_gemm_nt_masked_swiglu, a.data_ptr(), b.data_ptr(),
+         codes.data_ptr(), sf.data_ptr(), a_sf.data_ptr(), b_sf.data_ptr(), masked_m.data_ptr(),
+         G, M_max, I, K)
     return codes, sf
 
 
@@ -316,9 +325,8 @@ def quantize_fp8_1x128(x, codes=None, sf=None):
     _fp8(codes, "codes")
     _need(codes, "codes", codes.dtype, (M, K), dev)
     _need(sf, "sf", torch.float32, (M, K // BLOCK), dev)
-    with torch.cuda.device(dev):
-        check(lib.dg_quantize_fp8_1x128(x.data_ptr(), dtype, codes.data_ptr(), sf.data_ptr(),
-                                        M, K, _stream(dev)))
+    _run(dev, lib.dg_quantize_fp8_1x128, x.data_ptr(), dtype, codes.data_ptr(), sf.data_ptr(),
+         M, K)
     return codes, sf
 
 
