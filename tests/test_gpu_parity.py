@@ -291,6 +291,42 @@ def run_masked(A, B, sfA, sfB, masked_m, expected_m=None, seed=3):
     return out.result(), out.initial()
 
 
+def test_masked_partial_round_only():
+    # 6 live tiles on a 16-workgroup grid (4 experts x 2 M-tiles x 2 N-tiles at full
+    # height): the grid is mostly idle and one expert has a full 256-row pair of
+    # tiles; integer-valued operands, so the result is exact
+    rng = np.random.default_rng(41)
+    G, M_max, N, K = 4, 256, 512, 1024
+    masked_m = np.array([256, 0, 0, 10], dtype=np.int32)
+    A, B, sfA, sfB = int_operands(rng, G * M_max, N, K, G=G)
+    A, sfA = A.reshape(G, M_max, K), sfA.reshape(G, M_max, K // 128)
+    g, init = run_masked(A, B, sfA, sfB, masked_m)
+    r, produced = oracle.grouped_masked(A, B, sfA, sfB, masked_m)
+    assert np.array_equal(g[~produced], init[~produced]), "masked rows touched"
+    assert_bitwise(g[produced], r[produced], "masked partial round")
+
+
+def test_masked_one_round_and_two_tiles():
+    # 258 live tiles on the full 256-workgroup grid: one persistent round, then the
+    # last expert's 2 tiles on two workgroups alone; that expert is checked in full,
+    # the others at sampled positions; integer-valued operands
+    rng = np.random.default_rng(43)
+    G, M_max, N, K = 9, 2048, 512, 1024
+    masked_m = np.array([2048] * 8 + [100], dtype=np.int32)
+    A, B, sfA, sfB = int_operands(rng, G * M_max, N, K, G=G)
+    A, sfA = A.reshape(G, M_max, K), sfA.reshape(G, M_max, K // 128)
+    g, init = run_masked(A, B, sfA, sfB, masked_m)
+    e = 8
+    assert np.array_equal(g[e, 100:], init[e, 100:]), "masked rows touched"
+    assert_bitwise(g[e, :100], oracle.gemm_nt(A[e, :100], B[e], sfA[e, :100], sfB[e]),
+                   "masked, last expert")
+    ei = rng.integers(0, 8, 3000)
+    mi = rng.integers(0, M_max, 3000)
+    ni = rng.integers(0, N, 3000)
+    r = oracle.grouped_masked_at(A, B, sfA, sfB, masked_m, ei, mi, ni)
+    assert_bitwise(g[ei, mi, ni], r, "masked whole tiles, sampled")
+
+
 def test_masked_small_edges():
     masked_m = np.array([0, 200, 1, 129, 64, 65, 999, -4], dtype=np.int32)  # last two clamp
     w = synth.masked(8, 200, 256, 384, seed_base=990000, masked_m=masked_m,
