@@ -157,8 +157,9 @@ dg_status launch_pipe_swiglu(const Problem& p0, int64_t blocks, int64_t I, uint8
 
 // ---------------------------------------------------------------- split-K workspace
 //
-// Skinny launches with K split across workgroups keep fp32 partials and per-tile
-// arrival counters in library-owned device buffers, one set per (device, stream):
+// Launches that split K across workgroups (the M <= 64 kernels, the dense tail
+// split of the compute-bound kernel) keep fp32 partials and per-tile arrival
+// counters in library-owned device buffers, one set per (device, stream):
 // calls on one stream run in order and reuse them; calls on different streams never
 // share them. Every counter is zero between calls (zeroed when allocated, reset by
 // the kernel after use), so the counter buffer stays valid when a later call uses

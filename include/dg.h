@@ -21,6 +21,16 @@
  *  - Every pointer is DEVICE memory owned by the caller; the library never
  *    allocates, frees or keeps a user buffer. All matrices are row-major and
  *    dense (leading dimension = row length).
+ *  - Library-owned memory: some calls use device buffers that the library
+ *    allocates per (device, stream) the first time a call needs them (hipMalloc,
+ *    and a hipMemsetAsync that zeroes the counters):
+ *      - fp32 partial tiles and arrival counters, for calls that split K across
+ *        workgroups (the M <= 64 kernels, and the last partial round of tiles of a
+ *        larger dense GEMM);
+ *      - transposed operand copies, for the NN / TN / TT calls.
+ *    The buffers only grow and live until the process ends. Calls on one stream
+ *    share them in stream order; calls on different streams never share them. A
+ *    call that needs no larger buffer allocates nothing.
  *  - A and B hold e4m3fn codes (1 byte). "NT": both are K-contiguous, B is [N][K].
  *  - C is bf16 (2 bytes), written with one round-to-nearest-even from the fp32
  *    accumulator. Only the output rows the call produces are written.
