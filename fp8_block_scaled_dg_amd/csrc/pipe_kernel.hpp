@@ -164,6 +164,35 @@ __device__ __forceinline__ void pipe_issue(const PipeThread<Cfg>& th, int kb, in
 #endif
 }
 
+// Operand DMAs [LO, HI) of K-block kb's batch into stage S (op q < A_DMA: A op q,
+// else B op q - A_DMA), the scales first when SCALES and LO == 0: the batch of
+// pipe_issue, issued a few instructions at a time.
+template <class Cfg, int S, bool SCALES, int LO, int HI>
+__device__ __forceinline__ void pipe_issue_ops(const PipeThread<Cfg>& th, int kb, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (SCALES && LO == 0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sa_rsrc,
+                                             DG_LDS(pipe_scale + wave * kScaleWaveBytes), 12,
+                                             th.sa_off, (kb >> th.sa_shift) << 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sb_rsrc, DG_LDS(pipe_sfb), 12, th.sb_off, kb * 4,
+                                             0, 0);
+  }
+  uint8_t* st = pipe_stage<S>();
+  const int koff = kb * kKBlock;
+#pragma unroll
+  for (int q = LO; q < HI; ++q) {
+    if (q < Cfg::A_DMA)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(th.a_rsrc,
+                                               DG_LDS(st + (wave * Cfg::A_DMA + q) * 1024), 16,
+                                               th.a_off[q], koff, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          th.b_rsrc, DG_LDS(st + Cfg::OFF_B + (wave * Cfg::B_DMA + q - Cfg::A_DMA) * 1024), 16,
+          th.b_off[q - Cfg::A_DMA], koff, 0, 0);
+  }
+#endif
+}
+
 // Byte address of stage S for the fragment reads. Stages 0 and 1 start below 64 KB,
 // so their base folds into the 16-bit offset of ds_read; stage 2 starts above it
 // and is added at run time from an opaque SGPR, so that the compiler does not keep
@@ -315,11 +344,14 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   p01 = mfma32(f.c1, f.a1, p01);  // M4
   promote8<8>(acc[1][1], carry[1], carry_s);
   DG_FENCE();
-  // block kb+1 in LDS, block kb's stage free
+  // block kb+1 in LDS, block kb's stage free. Block kb+3's DMAs into it are spread
+  // over M5..M8 (each wave issues a few behind each MFMA instead of all eight
+  // waves queueing a whole batch at the address unit right after the barrier);
+  // all of them precede the next step's wait, so its count is unchanged.
+  constexpr int OPS = Cfg::OPS_PER_KB, Q1 = (OPS + 2) / 3, Q2 = (2 * OPS + 2) / 3;
+  const int kn = kb + 3 < KB ? kb + 3 : KB - 1;
   wait_vm_lgkm0<Cfg::OPS_PER_KB>();
   __builtin_amdgcn_s_barrier();
-  DG_FENCE();
-  pipe_issue<Cfg, S, S == 0>(th, kb + 3 < KB ? kb + 3 : KB - 1, wave);
   DG_FENCE();
   const float s0 = sc.s0[S], s1 = sc.s1[S];
   read_tile(nst, pl.va, 0, f.a0, f.a1);
@@ -327,12 +359,15 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   read_tile(nst, pl.vb, 1, c0n, c1n);
   DG_FENCE();
   v16f p10 = mfma32(f.b0, a10, zero);  // M5
+  pipe_issue_ops<Cfg, S, S == 0, 0, Q1>(th, kn, wave);
   promote8<0>(acc[0][0], p00, s0);
   DG_FENCE();
   v16f p11 = mfma32(f.c0, a10, zero);  // M6
+  pipe_issue_ops<Cfg, S, false, Q1, Q2>(th, kn, wave);
   promote8<8>(acc[0][0], p00, s0);
   DG_FENCE();
   p10 = mfma32(f.b1, a11, p10);  // M7
+  pipe_issue_ops<Cfg, S, false, Q2, OPS>(th, kn, wave);
   promote8<0>(acc[0][1], p01, s0);
   DG_FENCE();
   read_tile(nst, pl.vb, 0, f.b0, f.b1);
