@@ -355,11 +355,11 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   DG_FENCE();
   const float s0 = sc.s0[S], s1 = sc.s1[S];
   read_tile(nst, pl.va, 0, f.a0, f.a1);
-  v8i c0n, c1n;
-  read_tile(nst, pl.vb, 1, c0n, c1n);
   DG_FENCE();
   v16f p10 = mfma32(f.b0, a10, zero);  // M5
   pipe_issue_ops<Cfg, S, S == 0, 0, Q1>(th, kn, wave);
+  v8i c0n, c1n;
+  read_tile(nst, pl.vb, 1, c0n, c1n);
   promote8<0>(acc[0][0], p00, s0);
   DG_FENCE();
   v16f p11 = mfma32(f.c0, a10, zero);  // M6
