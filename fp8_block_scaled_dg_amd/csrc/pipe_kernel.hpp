@@ -345,9 +345,9 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   promote8<8>(acc[1][1], carry[1], carry_s);
   DG_FENCE();
   // block kb+1 in LDS, block kb's stage free. Block kb+3's DMAs into it are spread
-  // over M5..M8 (each wave issues a few behind each MFMA instead of all eight
-  // waves queueing a whole batch at the address unit right after the barrier);
-  // all of them precede the next step's wait, so its count is unchanged.
+  // over M5..M7, a third behind each (instead of all eight waves queueing a whole
+  // batch at the address unit right after the barrier); all of them precede the
+  // next step's wait, so its count is unchanged.
   constexpr int OPS = Cfg::OPS_PER_KB, Q1 = (OPS + 2) / 3, Q2 = (2 * OPS + 2) / 3;
   const int kn = kb + 3 < KB ? kb + 3 : KB - 1;
   wait_vm_lgkm0<Cfg::OPS_PER_KB>();
