@@ -345,10 +345,11 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   promote8<8>(acc[1][1], carry[1], carry_s);
   DG_FENCE();
   // block kb+1 in LDS, block kb's stage free. Block kb+3's DMAs into it are spread
-  // over M5..M7, a third behind each (instead of all eight waves queueing a whole
+  // over M5..M8, a quarter behind each (instead of all eight waves queueing a whole
   // batch at the address unit right after the barrier); all of them precede the
   // next step's wait, so its count is unchanged.
-  constexpr int OPS = Cfg::OPS_PER_KB, Q1 = (OPS + 2) / 3, Q2 = (2 * OPS + 2) / 3;
+  constexpr int OPS = Cfg::OPS_PER_KB, Q1 = (OPS + 3) / 4, Q2 = (2 * OPS + 3) / 4,
+                Q3 = (3 * OPS + 3) / 4;
   const int kn = kb + 3 < KB ? kb + 3 : KB - 1;
   wait_vm_lgkm0<Cfg::OPS_PER_KB>();
   __builtin_amdgcn_s_barrier();
@@ -367,12 +368,13 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   promote8<8>(acc[0][0], p00, s0);
   DG_FENCE();
   p10 = mfma32(f.b1, a11, p10);  // M7
-  pipe_issue_ops<Cfg, S, false, Q2, OPS>(th, kn, wave);
+  pipe_issue_ops<Cfg, S, false, Q2, Q3>(th, kn, wave);
   promote8<0>(acc[0][1], p01, s0);
   DG_FENCE();
   read_tile(nst, pl.vb, 0, f.b0, f.b1);
   DG_FENCE();
   p11 = mfma32(f.c1, a11, p11);  // M8
+  pipe_issue_ops<Cfg, S, false, Q3, OPS>(th, kn, wave);
   promote8<8>(acc[0][1], p01, s0);
   DG_FENCE();
   f.c0 = c0n;
