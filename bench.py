@@ -592,6 +592,23 @@ def summarize(manifest_path: str) -> None:
             lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
                          f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                          f"{float(r['MaxNs']) / 1e3:.2f} |")
+        # the timed region is each GEMM's last `steps` dispatches, launched back to back
+        trace = [r for r in _csv_rows(t["dir"], "kernel_trace.csv") if _ours(r["Kernel_Name"])]
+        per = {}
+        for r in trace:
+            per.setdefault(_short(r["Kernel_Name"]), []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        K = line["steps"]
+        lines += ["", f"Kernel trace of the timed region only (each kernel's last {K} "
+                      "dispatches); `span` is first start to last end over the dispatches, "
+                      "the launch-to-launch time:", "",
+                  "| kernel | dispatches | avg us | span us per dispatch |", "|---|---|---|---|"]
+        for k, ts in per.items():
+            ts.sort()
+            last = ts[-K:]
+            avg = sum(e - s for s, e in last) / len(last) / 1e3
+            span = (last[-1][1] - last[0][0]) / len(last) / 1e3
+            lines.append(f"| `{k}` | {len(last)} | {avg:.2f} | {span:.2f} |")
         lines += ["", "bench.py line of the same run (HIP events around each GEMM's "
                       "back-to-back launches):", ""]
         for k in line["kernels"]:
