@@ -573,11 +573,14 @@ struct SwigluOut {
 // features": Mega MoE fuses Linear1, SwiGLU and Linear2) is formed from the fp32
 // accumulators and quantized per 1x128 block (h's columns n0..n0+127 of a row are one
 // block) by the same rule as the activation quantizer, so the output is the next
-// GEMM's A and sfA:
-//   1. the up waves (wn = 2, 3) hand their 64x64 fp32 sub-tiles to the gate waves
-//      with the same lanes (wn - 2) through LDS (the stages are free by now);
-//   2. the gate waves form h = g / (1 + e^-g) * u in fp32 and each row's max |h| over
-//      their 64 columns; the two gate waves of a row half combine theirs through LDS;
+// GEMM's A and sfA. A gate wave (wn = 0, 1) and the up wave with the same lanes
+// (wn + 2) hold gate and up of the same 64 x 64 positions; each finishes one 32-row
+// half of them, so all eight waves share the work:
+//   1. the gate wave passes the gate values of rows 32..63 to its up wave, which
+//      passes the up values of rows 0..31 back, through LDS (the stages are free);
+//   2. each wave forms h = g / (1 + e^-g) * u in fp32 for its 32 x 64 values and each
+//      row's max |h| over them; the two waves that share a row's 128 columns combine
+//      theirs through LDS;
 //   3. codes of h * 2^-e go to an LDS tile, the scale 2^e straight to sf;
 //   4. all threads store the tile's produced rows with 16-byte stores.
 template <class Cfg, int KIND>
@@ -586,66 +589,59 @@ __device__ __forceinline__ void pipe_store_swiglu(const Problem& p, const TileVi
                                                   v16f (&acc)[Cfg::TM][Cfg::TN],
                                                   const SwigluOut& out) {
   static_assert(Cfg::BM == 128 && Cfg::BN == 256, "gate and up halves of 128 columns");
-  constexpr int TM = Cfg::TM, TN = Cfg::TN;
+  constexpr int TN = Cfg::TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
   const int r32 = lane & 31, g = lane >> 5;
+  const bool up = wn >= 2;
+  const int ih = up ? 1 : 0;  // the 32-row half (tile row) this wave finishes
   const int slot = wm * 2 + (wn & 1);
   float* xch = (float*)((slot < 2 ? pipe_stage0 : pipe_stage1) + (slot & 1) * 16384);
-  float* rmax_lds = (float*)pipe_scale;   // [wm * 2 + wn][64 rows]
-  uint8_t* codes_lds = pipe_stage2;       // [128 rows][128 columns]
-  if (wn >= 2) {
+  float* give = xch + (up ? 0 : 2048);  // up values of half 0 | gate values of half 1
+  const float* take = xch + (up ? 2048 : 0);
+  float* rmax_lds = (float*)pipe_scale;  // [wm * 2 + (wn & 1)][64 rows]
+  uint8_t* codes_lds = pipe_stage2;      // [128 rows][128 columns]
+  // (selects, not acc[ih]: a run-time index would move acc out of registers)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) xch[((i * TN + j) * 16 + e) * 64 + lane] = acc[i][j][e];
-  }
+    for (int e = 0; e < 16; ++e) give[(j * 16 + e) * 64 + lane] = up ? acc[0][j][e] : acc[1][j][e];
   __syncthreads();
-  if (wn < 2) {
-    float rm[TM];
+  float hv[TN][16];
+  float rm = 0.f;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      rm[i] = 0.f;
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float gt = acc[i][j][e], up = xch[((i * TN + j) * 16 + e) * 64 + lane];
-          const float h = gt / (1.f + expf(-gt)) * up;
-          acc[i][j][e] = h;
-          rm[i] = fmaxf(rm[i], fabsf(h));
-        }
-      rm[i] = fmaxf(rm[i], __shfl_xor(rm[i], 32, 64));
-      if (g == 0) rmax_lds[(wm * 2 + wn) * 64 + i * 32 + r32] = rm[i];
+    for (int e = 0; e < 16; ++e) {
+      const float mine = up ? acc[1][j][e] : acc[0][j][e];
+      const float other = take[(j * 16 + e) * 64 + lane];
+      const float gt = up ? other : mine, u = up ? mine : other;
+      // g / (1 + e^-g) as g * rcp(1 + e^-g): 1 ulp reciprocal, no division sequence
+      const float h = gt * __builtin_amdgcn_rcpf(1.f + expf(-gt)) * u;
+      hv[j][e] = h;
+      rm = fmaxf(rm, fabsf(h));
     }
-  }
+  rm = fmaxf(rm, __shfl_xor(rm, 32, 64));  // lanes r32 and r32 + 32 share a row
+  if (g == 0) rmax_lds[slot * 64 + ih * 32 + r32] = rm;
   __syncthreads();
-  if (wn < 2) {
+  {
+    const int rl = wm * 64 + ih * 32 + r32;  // row within the tile
+    const float m = fmaxf(rmax_lds[(wm * 2) * 64 + ih * 32 + r32],
+                          rmax_lds[(wm * 2 + 1) * 64 + ih * 32 + r32]);
+    const int e = quant_scale_exp(m);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int rl = wm * 64 + i * 32 + r32;  // row within the tile
-      const float m = fmaxf(rmax_lds[(wm * 2) * 64 + i * 32 + r32],
-                            rmax_lds[(wm * 2 + 1) * 64 + i * 32 + r32]);
-      const int e = quant_scale_exp(m);
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            w |= quant_e4m3fn(ldexpf(acc[i][j][4 * q + t], -e)) << (8 * t);
-          *(uint32_t*)(codes_lds + rl * 128 + wn * 64 + j * 32 + 8 * q + 4 * g) = w;
-        }
-      if (wn == 0 && g == 0) {
-        const int64_t row = v.m0 + rl;
-        bool ok = row < (int64_t)valid_rows;
-        if (KIND == kContiguous && ok) ok = p.m_indices[row] == expert;
-        if (ok) out.sf[row * (out.I / 128) + v.n0 / 128] = ldexpf(1.f, e);
-      }
+      for (int q = 0; q < 4; ++q)
+        *(uint32_t*)(codes_lds + rl * 128 + (wn & 1) * 64 + j * 32 + 8 * q + 4 * g) =
+            quant_e4m3fn_x4(ldexpf(hv[j][4 * q], -e), ldexpf(hv[j][4 * q + 1], -e),
+                            ldexpf(hv[j][4 * q + 2], -e), ldexpf(hv[j][4 * q + 3], -e));
+    if ((wn & 1) == 0 && g == 0) {
+      const int64_t row = v.m0 + rl;
+      bool ok = row < (int64_t)valid_rows;
+      if (KIND == kContiguous && ok) ok = p.m_indices[row] == expert;
+      if (ok) out.sf[row * (out.I / 128) + v.n0 / 128] = ldexpf(1.f, e);
     }
   }
   __syncthreads();
