@@ -573,11 +573,54 @@ def _per_dispatch(folder: str, counter: str):
     return {k: acc[k] / len(disp[k]) for k in acc}, {k: len(v) for k, v in disp.items()}
 
 
+def _summarize_counters(entries, out_dir: str) -> None:
+    """MFMA busy fraction per compute-bound workload from SQ_VALU_MFMA_BUSY_CYCLES
+    (summed over every SIMD; 64 per 32x32x64 FP8 MFMA) and GRBM_GUI_ACTIVE (summed
+    over the XCCs), averaged over our kernel's dispatches."""
+    agent = [r for r in _csv_rows(entries[0]["dir"], "agent_info.csv") if r["Agent_Type"] == "GPU"][0]
+    simds, xcc = int(agent["Simd_Count"]), int(agent["Num_Xcc"])
+    clk = float(agent["Max_Engine_Clk_Fcompute"]) / 1e3
+    md = ["# MFMA utilisation (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE)", "",
+          f"GPU: {agent['Name']}, {simds} SIMDs, {xcc} XCCs, {clk:.1f} GHz peak engine clock. "
+          "busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCC x SIMDs), the rocprofv3 "
+          "MfmaUtil expression; MFMAs = busy cycles / 64 (one 32x32x64 FP8 MFMA keeps a SIMD's "
+          "matrix unit busy 64 cycles); clock = GRBM_GUI_ACTIVE per XCC / dispatch duration; "
+          "busy x clock / peak clock is the fraction of the FP8 peak the MFMA work reaches. "
+          "GRBM_GUI_ACTIVE spans slightly more than the kernel (launch and drain), so the clock "
+          "reads a little high on the shorter kernels.", "",
+          "| workload | dispatches | MFMAs issued | algorithmic MFMAs | busy | clock GHz | busy x clock/peak |",
+          "|---|---|---|---|---|---|---|"]
+    for e in entries:
+        rows = [r for r in _csv_rows(e["dir"], "counter_collection.csv") if _ours(r["Kernel_Name"])]
+        val, disp, dur = {}, set(), {}
+        for r in rows:
+            val.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            disp.add(r["Dispatch_Id"])
+            dur[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+        busy = sum(val["SQ_VALU_MFMA_BUSY_CYCLES"]) / len(val["SQ_VALU_MFMA_BUSY_CYCLES"])
+        gui = sum(val["GRBM_GUI_ACTIVE"]) / len(val["GRBM_GUI_ACTIVE"]) / xcc
+        t = sum(dur.values()) / len(dur)
+        util = busy / (gui * simds)
+        ghz = gui / t / 1e9
+        bj = e["dir"] + ".json"
+        bj = bj if os.path.isabs(bj) else os.path.join(ROOT, bj)
+        with open(bj) as f:
+            line = json.loads([x for x in f.read().splitlines() if x.startswith("{")][-1])
+        alg = sum(k["alg_flops"] for k in line["kernels"]) / (2 * 32 * 32 * 64)
+        md.append(f"| {e['label']} | {len(disp)} | {busy / 64:.4g} | {alg:.4g} | {util:.3f} | "
+                  f"{ghz:.2f} | {util * ghz / clk:.3f} |")
+    md += ["", "Commands (repository root on the GPU host):", ""]
+    md += ["    " + e["command"] for e in entries]
+    with open(os.path.join(out_dir, "counters_mfma.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
 def summarize(manifest_path: str) -> None:
     with open(manifest_path) as f:
         man = json.load(f)
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
+    timed = {}  # workload -> kernel -> timed-region average us
     for t in man.get("trace", []):
         stats = [r for r in _csv_rows(t["dir"], "kernel_stats.csv") if _ours(r["Name"])]
         bj = t["bench_json"] if os.path.isabs(t["bench_json"]) else os.path.join(ROOT, t["bench_json"])
@@ -609,6 +652,7 @@ def summarize(manifest_path: str) -> None:
             avg = sum(e - s for s, e in last) / len(last) / 1e3
             span = (last[-1][1] - last[0][0]) / len(last) / 1e3
             lines.append(f"| `{k}` | {len(last)} | {avg:.2f} | {span:.2f} |")
+            timed.setdefault(t["label"], {})[k] = avg
         lines += ["", "bench.py line of the same run (HIP events around each GEMM's "
                       "back-to-back launches):", ""]
         for k in line["kernels"]:
@@ -617,6 +661,9 @@ def summarize(manifest_path: str) -> None:
                   f"roofline frac {line['roofline']['frac']:.3f}", ""]
         with open(os.path.join(out_dir, f"trace_{t['label']}.md"), "w") as f:
             f.write("\n".join(lines))
+    cn = man.get("counters")
+    if cn:
+        _summarize_counters(cn, out_dir)
     tr = man.get("traffic")
     if tr:
         cal = tr["calibration"]
@@ -644,8 +691,8 @@ def summarize(manifest_path: str) -> None:
               f"(kernel `{_short(kern)}`); scale factors fetch {f_scale:.4f}, "
               f"write {w_scale:.4f}.", "",
               "    " + cal["command_fetch"], "    " + cal["command_write"], "",
-              "| GEMM | kernel | dispatches | fetch KiB | write KiB | scaled bytes |",
-              "|---|---|---|---|---|---|"]
+              "| GEMM | kernel | dispatches | fetch KiB | write KiB | scaled bytes | kernel us | HBM GB/s |",
+              "|---|---|---|---|---|---|---|---|"]
         for g in tr["gemms"]:
             fv, fn = _per_dispatch(g["fetch"], "FETCH_SIZE")
             wv, _ = _per_dispatch(g["write"], "WRITE_SIZE")
@@ -659,9 +706,15 @@ def summarize(manifest_path: str) -> None:
                                         "write_kib": wv.get(k, 0.0), "dispatches": fn[k],
                                         "command_fetch": g["command_fetch"],
                                         "command_write": g["command_write"]}
+            us = timed.get(g["workload"], {}).get(_short(k))
+            rate = f"{us:.1f} | {b / (us * 1e-6) / 1e9:.0f}" if us else "- | -"
             md.append(f"| {g['gemm']} | `{_short(k)}` | {fn[k]} | {fv[k]:.0f} | "
-                      f"{wv.get(k, 0.0):.0f} | {b:.4g} |")
+                      f"{wv.get(k, 0.0):.0f} | {b:.4g} | {rate} |")
             md += ["", "    " + g["command_fetch"], "    " + g["command_write"], ""]
+        md.append("kernel us: the kernel trace's timed-region average of the same workload "
+                  "(trace_*.md); HBM GB/s: scaled bytes / kernel us, the rate the L2 misses and "
+                  "write-backs reach (partials of split-K included), against 8 TB/s.")
+        md.append("")
         md.append(f"kernel sources: {rec['kernel_source']}")
         with open(os.path.join(out_dir, "traffic.json"), "w") as f:
             json.dump(rec, f, indent=1)
