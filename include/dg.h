@@ -183,7 +183,8 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const void* A, const void* B, vo
  * (masked, as [G][M_max][...], masked_m as in the masked GEMM). For each produced
  * row, with g and u the fp32 block-scaled products of the gate and up columns
  * (two-level accumulation as in the GEMM calls):
- *   h[j] = silu(g[j]) * u[j],  silu(x) = x / (1 + e^-x), in fp32;
+ *   h[j] = silu(g[j]) * u[j],  silu(x) = x / (1 + e^-x), in fp32 (the division as
+ *   a multiplication by the 1-ulp hardware reciprocal: h within a few ulps);
  * then h is quantized per 1x128 block exactly as dg_quantize_fp8_1x128 quantizes its
  * input: these outputs are the next GEMM's A operand and sfA. Rows that are not
  * produced (pad rows, rows >= masked_m[e]) are not written in codes or sf.
