@@ -398,6 +398,38 @@ def test_masked_workload_sampled():
     print("moe_mask sampled:", rep)
 
 
+# ------------------------------------------------------------------ longest K
+
+
+@pytest.mark.parametrize("M,K,cfg", [
+    (130, 1 << 22, "pipe256x128"),  # the pipelined kernels' longest K (32-bit row offsets)
+    (130, 1 << 22, "pipe128x256"),
+    (64, 1 << 22, None),            # M <= 64: the split-K decode kernel
+    (130, (1 << 22) + 128, None),   # one K-block past it: the generic tile kernel
+])
+def test_longest_k_sparse_blocks_bitwise(M, K, cfg, force_config):
+    """Integer operands in five K-blocks (both ends and the middle), zeros elsewhere:
+    every operand and scale address up to the last byte of the longest rows is read.
+    Zero blocks add exact zeros, so the oracle runs on the five blocks alone."""
+    if cfg:
+        force_config(cfg)
+    N, KB = 48, K // 128
+    blocks = [0, 1, KB // 2, KB - 2, KB - 1]
+    rng = np.random.default_rng(M + KB)
+    a, b, sa, sb = int_operands(rng, M, N, 128 * len(blocks))
+    A = np.zeros((M, K), np.uint8)
+    B = np.zeros((N, K), np.uint8)
+    sfA = np.ones((M, KB), np.float32)
+    sfB = np.ones(((N + 127) // 128, KB), np.float32)
+    for i, kb in enumerate(blocks):
+        A[:, kb * 128:(kb + 1) * 128] = a[:, i * 128:(i + 1) * 128]
+        B[:, kb * 128:(kb + 1) * 128] = b[:, i * 128:(i + 1) * 128]
+        sfA[:, kb] = sa[:, i]
+        sfB[:, kb] = sb[:, i]
+    g = run_dense(A, B, sfA, sfB)
+    assert_bitwise(g, oracle.gemm_nt(a, b, sa, sb), what=f"{cfg} {M}x{N}x{K}")
+
+
 # ------------------------------------------------------------------ every configuration
 
 
