@@ -615,6 +615,42 @@ def _summarize_counters(entries, out_dir: str) -> None:
         f.write("\n".join(md) + "\n")
 
 
+def _summarize_operand_path(passes, out_dir: str) -> None:
+    """Where the compute-bound kernel's cycles go on the operand path: TA (address) and
+    TD (data return) busy per CU, TD stalled on the texture cache, wave-cycles spent in
+    s_waitcnt, LDS bank conflicts; counters averaged over our kernel's dispatches and
+    normalised by GRBM_GUI_ACTIVE per XCC."""
+    agent = [r for r in _csv_rows(passes[0]["dir"], "agent_info.csv") if r["Agent_Type"] == "GPU"][0]
+    cus, xcc, ses = int(agent["Cu_Count"]), int(agent["Num_Xcc"]), int(agent["Num_Shader_Banks"])
+    vals = {}
+    for e in passes:
+        d = {}
+        for r in _csv_rows(e["dir"], "counter_collection.csv"):
+            if _ours(r["Kernel_Name"]):
+                d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for k, v in d.items():
+            vals.setdefault(e["label"], {})[(e["pass"], k)] = sum(v) / len(v)
+    md = ["# Operand path of the compute-bound kernel (rocprofv3 TA / TD / SQ counters)", "",
+          f"Per-CU blocks are normalised by GRBM_GUI_ACTIVE per XCC x {cus} CUs, the LDS command "
+          f"FIFO by GRBM_GUI_ACTIVE per XCC x {ses} shader engines; wave figures are fractions of "
+          "SQ_WAVE_CYCLES (both in quad-cycles), bank conflicts a fraction of SQ_LDS_IDX_ACTIVE.", "",
+          "| workload | TA busy | TD busy | TD stalled on TC | waves in s_waitcnt | waves waiting on LDS | "
+          "LDS cmd FIFO full | LDS bank conflicts |", "|---|---|---|---|---|---|---|---|"]
+    for wl, v in vals.items():
+        gui = v[("B", "GRBM_GUI_ACTIVE")] / xcc
+        per_cu = lambda k: v[("B", k)] / (gui * cus)
+        wave = v[("A", "SQ_WAVE_CYCLES")]
+        md.append(f"| {wl} | {per_cu('TA_TA_BUSY_sum'):.2f} | {per_cu('TD_TD_BUSY_sum'):.2f} | "
+                  f"{per_cu('TD_TC_STALL_sum'):.2f} | {v[('A', 'SQ_WAIT_INST_ANY')] / wave:.2f} | "
+                  f"{v[('A', 'SQ_WAIT_INST_LDS')] / wave:.2f} | "
+                  f"{v[('B', 'SQ_LDS_CMD_FIFO_FULL')] / (gui * ses):.2f} | "
+                  f"{v[('A', 'SQ_LDS_BANK_CONFLICT')] / v[('A', 'SQ_LDS_IDX_ACTIVE')]:.3f} |")
+    md += ["", "Commands (repository root on the GPU host):", ""]
+    md += ["    " + e["command"] for e in passes]
+    with open(os.path.join(out_dir, "counters_operand_path.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
 def summarize(manifest_path: str) -> None:
     with open(manifest_path) as f:
         man = json.load(f)
@@ -664,6 +700,9 @@ def summarize(manifest_path: str) -> None:
     cn = man.get("counters")
     if cn:
         _summarize_counters(cn, out_dir)
+    ps = man.get("passes")
+    if ps:
+        _summarize_operand_path(ps, out_dir)
     tr = man.get("traffic")
     if tr:
         cal = tr["calibration"]
