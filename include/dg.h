@@ -30,7 +30,8 @@
  *      - transposed operand copies, for the NN / TN / TT calls.
  *    The buffers only grow and live until the process ends. Calls on one stream
  *    share them in stream order; calls on different streams never share them. A
- *    call that needs no larger buffer allocates nothing.
+ *    call that needs no larger buffer allocates nothing, so a call may be captured
+ *    into a HIP graph once the same shape has run on that stream outside capture.
  *  - A and B hold e4m3fn codes (1 byte). "NT": both are K-contiguous, B is [N][K].
  *  - C is bf16 (2 bytes), written with one round-to-nearest-even from the fp32
  *    accumulator. Only the output rows the call produces are written.
