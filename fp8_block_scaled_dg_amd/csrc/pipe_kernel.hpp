@@ -510,11 +510,13 @@ __device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& 
 // L2 would take every one as a partial-line write. Instead each wave passes its
 // 64x64 sub-tile through its own 4 KB of LDS stage 2, 32 rows at a time, and reads
 // it back with 8 lanes per row: each store instruction then writes 8 whole 128-byte
-// row segments, an eighth of the write requests. Stage 2 is refilled only after the
-// barrier that follows the next tile's first DMAs, which a wave reaches after its
-// store. 16-byte chunk q of staged row r sits at chunk q ^ (r & 7), which spreads
-// both the writes (8-byte halves of one chunk column from 32 rows) and the reads
-// (a whole row per 8 lanes) evenly over the banks.
+// row segments, an eighth of the write requests. The stores are non-temporal: C is
+// not read again by this kernel, and keeping it out of L2 leaves room for A and B.
+// Stage 2 is refilled only after the barrier that follows the next tile's first
+// DMAs, which a wave reaches after its store. 16-byte chunk q of staged row r sits
+// at chunk q ^ (r & 7), which spreads both the writes (8-byte halves of one chunk
+// column from 32 rows) and the reads (a whole row per 8 lanes) evenly over the
+// banks.
 template <class Cfg, int KIND>
 __device__ __forceinline__ void pipe_store(const Problem& p, const TileView& v, int expert,
                                            int valid_rows, const v16f (&acc)[Cfg::TM][Cfg::TN]) {
@@ -553,7 +555,7 @@ __device__ __forceinline__ void pipe_store(const Problem& p, const TileView& v, 
       const int64_t row = v.m0 + wm * 64 + i * 32 + r;
       bool ok = row < (int64_t)valid_rows && col < N;
       if (KIND == kContiguous && ok) ok = p.m_indices[row] == expert;
-      if (ok) *(v4u*)(v.C + row * N + col) = d;
+      if (ok) __builtin_nontemporal_store(d, (v4u*)(v.C + row * N + col));
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   }

@@ -308,7 +308,8 @@ __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
   for (int c = tid; c < CH; c += NT) {
     const int row = c / (BN / 8), col0 = (c - row * (BN / 8)) * 8;
     if (row < M && n0 + col0 < N)
-      *(uint4*)(p.C + (int64_t)row * N + n0 + col0) = *(const uint4*)(stream_out + row * BN + col0);
+      __builtin_nontemporal_store(*(const v4u*)(stream_out + row * BN + col0),  // C is not read again
+                                  (v4u*)(p.C + (int64_t)row * N + n0 + col0));
   }
 }
 
