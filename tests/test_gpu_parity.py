@@ -5,9 +5,8 @@ oracle, element by element on the same seeded inputs.
 * integer-exact inputs (codes decoding to small integers, power-of-two scales):
   every block partial and every accumulation step is exact in fp32, so the GPU must
   equal the oracle's bf16 rounding bitwise -- this pins all indexing;
-* the full workload shapes, in the launch configuration the benchmark times:
-  every output where the oracle is fast enough, sampled outputs (all tile and
-  scale-block boundaries plus seeded random positions) where it is not;
+* the full workload shapes: the decode shapes here, prefill and the MoE
+  workloads in tests/test_gpu_full.py, every output in both;
 * rows a grouped call must not produce keep their seeded sentinel bytes, and 64 KB
   guard bands around every output stay intact.
 """
@@ -18,7 +17,7 @@ import torch
 import oracle
 import synth
 from tests import gpu_util as gu
-from tests.parity import assert_bitwise, assert_parity, report
+from tests.parity import abs_product_sum, assert_bitwise, assert_error_model, assert_parity, report
 
 pytestmark = pytest.mark.gpu
 
@@ -50,24 +49,6 @@ def run_dense(A, B, sfA, sfB, seed=1):
     torch.cuda.synchronize()
     assert out.guards_intact(), "write outside C"
     return out.result()
-
-
-def sample_positions(rng, M, N, n_random=4000, tile=(64, 128)):
-    rows = set([0, M - 1])
-    for t in tile:
-        for b in range(0, M, t):
-            rows.update([b, b - 1, b + 1])
-    cols = set([0, N - 1])
-    for b in range(0, N, 16):
-        if b % 128 == 0 or b % 64 == 0:
-            cols.update([b, b - 1, b + 15, b + 16])
-    rows = np.array(sorted(r for r in rows if 0 <= r < M))
-    cols = np.array(sorted(c for c in cols if 0 <= c < N))
-    # every boundary row against a spread of columns, every boundary column
-    # against a spread of rows, plus random positions
-    rr = [np.repeat(rows, 16), rng.integers(0, M, cols.size * 8), rng.integers(0, M, n_random)]
-    cc = [rng.integers(0, N, rows.size * 16), np.repeat(cols, 8), rng.integers(0, N, n_random)]
-    return np.concatenate(rr).astype(np.int64), np.concatenate(cc).astype(np.int64)
 
 
 # ------------------------------------------------------------------ dense
@@ -165,8 +146,11 @@ def test_dense_deterministic():
 def test_decode_workloads_full(name):
     w = synth.workload(name)
     g = run_dense(w.A, w.B, w.sfA, w.sfB)
-    rep = assert_parity(g, oracle.gemm_nt(w.A, w.B, w.sfA, w.sfB), what=name)
+    r = oracle.gemm_nt(w.A, w.B, w.sfA, w.sfB)
+    rep = assert_parity(g, r, what=name)
     print(name, rep)
+    model = assert_error_model(g, r, abs_product_sum(w.A, w.B, w.sfA, w.sfB), what=name)
+    print(name, "error model:", model)
 
 
 def test_decode_workloads_integer_exact_bitwise():
@@ -175,29 +159,6 @@ def test_decode_workloads_integer_exact_bitwise():
         A, B, sfA, sfB = int_operands(rng, M, N, K)
         g = run_dense(A, B, sfA, sfB)
         assert_bitwise(g, oracle.gemm_nt(A, B, sfA, sfB), what=f"int {M}x{N}x{K}")
-
-
-def test_prefill_workload_sampled():
-    w = synth.workload("prefill")
-    M, N, K = w.shape
-    g = run_dense(w.A, w.B, w.sfA, w.sfB)
-    rng = np.random.default_rng(99)
-    mi, ni = sample_positions(rng, M, N)
-    r = oracle.gemm_nt_at(w.A, w.B, w.sfA, w.sfB, mi, ni)
-    rep = assert_parity(g[mi, ni], r, what="prefill sampled")
-    print("prefill sampled:", rep)
-
-
-def test_prefill_integer_exact_sampled_bitwise():
-    M, N, K = 4096, 7168, 18432
-    rng = np.random.default_rng(4096)
-    A = rng.choice(INT_CODES, size=(M, K)).astype(np.uint8)
-    B = rng.choice(INT_CODES, size=(N, K)).astype(np.uint8)
-    sfA = np.ones((M, K // 128), dtype=np.float32)
-    sfB = np.ones((N // 128, K // 128), dtype=np.float32)
-    g = run_dense(A, B, sfA, sfB)
-    mi, ni = sample_positions(rng, M, N, n_random=2000)
-    assert_bitwise(g[mi, ni], oracle.gemm_nt_at(A, B, sfA, sfB, mi, ni), "prefill int")
 
 
 # ------------------------------------------------------------------ contiguous
@@ -253,26 +214,6 @@ def test_contiguous_nan_pad_rows_never_read():
     assert np.any(w.A == synth.FP8_NAN_CODE)
     g, init = run_contiguous(w.A, w.B, w.sfA, w.sfB, w.m_indices)
     check_contiguous_full(w, g, init)
-
-
-def test_contiguous_workload_sampled():
-    w = synth.workload("moe_cont")
-    M_total, N, K, G = w.shape
-    g, init = run_contiguous(w.A, w.B, w.sfA, w.sfB, w.m_indices)
-    pad = w.m_indices < 0
-    assert np.array_equal(g[pad], init[pad]), "pad rows touched"
-    rng = np.random.default_rng(7)
-    real_rows = np.nonzero(~pad)[0]
-    ri, ni = sample_positions(rng, real_rows.size, N)
-    ri = real_rows[ri]
-    # add the first and last row of every segment
-    firsts = [np.nonzero(w.m_indices == e)[0] for e in range(G) if w.counts[e] > 0]
-    edge = np.concatenate([[s[0], s[-1]] for s in firsts])
-    ri = np.concatenate([ri, np.repeat(edge, 32)])
-    ni = np.concatenate([ni, rng.integers(0, N, edge.size * 32)])
-    r = oracle.grouped_contiguous_at(w.A, w.B, w.sfA, w.sfB, w.m_indices, ri, ni)
-    rep = assert_parity(g[ri, ni], r, what="moe_cont sampled")
-    print("moe_cont sampled:", rep)
 
 
 # ------------------------------------------------------------------ masked
@@ -373,29 +314,6 @@ def test_masked_all_empty_untouched():
     A, sfA = A.reshape(G, M_max, K), sfA.reshape(G, M_max, K // 128)
     g, init = run_masked(A, B, sfA, sfB, np.array([0, -3, 0, 0, 0], dtype=np.int32))
     assert np.array_equal(g, init), "an all-empty call wrote output"
-
-
-def test_masked_workload_sampled():
-    w = synth.workload("moe_mask", pad_code=synth.FP8_NAN_CODE)
-    G, M_max, N, K = w.shape
-    g, init = run_masked(w.A, w.B, w.sfA, w.sfB, w.masked_m)
-    produced = np.arange(M_max)[None, :] < w.masked_m[:, None]
-    assert np.array_equal(g[~produced], init[~produced]), "masked rows touched"
-    rng = np.random.default_rng(8)
-    e_all, m_all = np.nonzero(produced)
-    pick = rng.integers(0, e_all.size, 6000)
-    ei, mi = e_all[pick], m_all[pick]
-    ni = rng.integers(0, N, pick.size)
-    # last valid row of every expert, and column block edges
-    last = [(e, w.masked_m[e] - 1) for e in range(G) if w.masked_m[e] > 0]
-    le = np.repeat([x[0] for x in last], 16)
-    lm = np.repeat([x[1] for x in last], 16)
-    ln = np.tile(np.array([0, 127, 128, 255, 256, 1023, 1024, N - 129, N - 128, N - 1,
-                           64, 63, 2047, 2048, 4095, 4096]), len(last))
-    ei, mi, ni = (np.concatenate([ei, le]), np.concatenate([mi, lm]), np.concatenate([ni, ln]))
-    r = oracle.grouped_masked_at(w.A, w.B, w.sfA, w.sfB, w.masked_m, ei, mi, ni)
-    rep = assert_parity(g[ei, mi, ni], r, what="moe_mask sampled")
-    print("moe_mask sampled:", rep)
 
 
 # ------------------------------------------------------------------ longest K
