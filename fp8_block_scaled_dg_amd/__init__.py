@@ -33,13 +33,31 @@ LIB_PATH = os.path.join(_PKG, "libdg.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m fp8_block_scaled_dg_amd.build` (hipcc, gfx950)")
+        f"{LIB_PATH} is not built; run `python fp8_block_scaled_dg_amd/build.py` (hipcc, gfx950)")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 
 lib = ctypes.CDLL(LIB_PATH)
+lib.dg_build_id.restype = ctypes.c_char_p
+lib.dg_build_id.argtypes = []
+BUILD_ID = lib.dg_build_id().decode()
+
+
+def _check_current() -> None:
+    """Refuse a libdg.so built from other sources than the ones beside it."""
+    from . import build as _build
+    try:
+        want = _build.source_hash()
+    except OSError:  # sources not shipped: nothing to compare with
+        return
+    if want != BUILD_ID:
+        raise ImportError(f"{LIB_PATH} was built from other sources (build id {BUILD_ID}, "
+                          f"sources {want}); rebuild it: python fp8_block_scaled_dg_amd/build.py")
+
+
+_check_current()
 lib.dg_fp8_gemm_nt.restype = ctypes.c_int
 lib.dg_fp8_gemm_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 lib.dg_m_grouped_fp8_gemm_nt_contiguous.restype = ctypes.c_int
@@ -74,6 +92,8 @@ for _name in ("dg_fp8_gemm_nn", "dg_fp8_gemm_tn", "dg_fp8_gemm_tt"):
 lib.dg_quantize_fp8_1x128.restype = ctypes.c_int
 lib.dg_quantize_fp8_1x128.argtypes = [_vp, _i32, _vp, _vp, _i64, _i64, _vp]
 
+lib.dg_release_workspaces.restype = ctypes.c_int
+lib.dg_release_workspaces.argtypes = []
 lib.dg_num_configs.restype = _i32
 lib.dg_num_configs.argtypes = []
 lib.dg_config_name.restype = ctypes.c_char_p
@@ -330,6 +350,13 @@ def quantize_fp8_1x128(x, codes=None, sf=None):
     return codes, sf
 
 
+def release_workspaces() -> None:
+    """Free the library's own device buffers (split-K partials and counters, transposed
+    operand copies) after the devices holding them go idle. No HIP graph holding a
+    library call may be replayed afterwards."""
+    check(lib.dg_release_workspaces())
+
+
 def describe_config(kind: int, M: int, N: int, K: int, G: int = 1, expected_m: int = 0) -> str:
     buf = ctypes.create_string_buffer(128)
     check(lib.dg_describe_config(kind, M, N, K, G, expected_m, buf, 128))
@@ -342,4 +369,4 @@ def config_names() -> list[str]:
 
 __all__ = ["config_names", "fp8_gemm_nt", "fp8_gemm_nn", "fp8_gemm_tn", "fp8_gemm_tt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
            "m_grouped_fp8_gemm_nt_contiguous_swiglu", "m_grouped_fp8_gemm_nt_masked_swiglu",
-           "quantize_fp8_1x128", "describe_config", "DGError", "lib", "LIB_PATH"]
+           "quantize_fp8_1x128", "describe_config", "release_workspaces", "BUILD_ID", "DGError", "lib", "LIB_PATH"]

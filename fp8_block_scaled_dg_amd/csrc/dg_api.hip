@@ -18,6 +18,7 @@
 #include <set>
 #include <string>
 #include <tuple>
+#include <vector>
 
 #include "../../include/dg.h"
 #include "gemm_kernel.hpp"
@@ -163,8 +164,11 @@ dg_status launch_pipe_swiglu(const Problem& p0, int64_t blocks, int64_t I, uint8
 // calls on one stream run in order and reuse them; calls on different streams never
 // share them. Every counter is zero between calls (zeroed when allocated, reset by
 // the kernel after use), so the counter buffer stays valid when a later call uses
-// more of it. Buffers only grow (an outgrown one is released in stream order) and
-// live until the process ends.
+// more of it. Buffers only grow. An outgrown buffer is not freed but retired: a HIP
+// graph captured earlier may still point at it, so it stays allocated until
+// dg_release_workspaces() or the end of the process. A call that would have to
+// grow a buffer while its stream is being captured returns DG_ERR_CAPTURE instead
+// of allocating (and zeroing) inside the capture.
 struct Workspace {
   void* partials = nullptr;
   size_t partial_bytes = 0;
@@ -174,22 +178,36 @@ struct Workspace {
   size_t a_t_bytes = 0;
   void* b_t = nullptr;
   size_t b_t_bytes = 0;
+  std::vector<void*> retired;
 };
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-dg_status grow(void** buf, size_t* have, size_t need, size_t elem, hipStream_t stream, bool zero) {
+dg_status grow(Workspace& w, void** buf, size_t* have, size_t need, size_t elem,
+               hipStream_t stream, bool zero) {
   if (*have >= need) return DG_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess)
+    return fail(DG_ERR_LAUNCH, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(DG_ERR_CAPTURE,
+                "the stream is being captured and this shape needs a larger library "
+                "workspace (%zu bytes); run the call once on this stream outside capture first",
+                need * elem);
   void* fresh = nullptr;
-  hipError_t e = hipMalloc(&fresh, need * elem);
+  e = hipMalloc(&fresh, need * elem);
   if (e != hipSuccess)
     return fail(DG_ERR_LAUNCH, "workspace hipMalloc(%zu): %s", need * elem, hipGetErrorString(e));
   if (zero) {
     e = hipMemsetAsync(fresh, 0, need * elem, stream);
-    if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "workspace clear: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+      (void)hipFree(fresh);
+      return fail(DG_ERR_LAUNCH, "workspace clear: %s", hipGetErrorString(e));
+    }
   }
-  if (*buf) (void)hipFreeAsync(*buf, stream);
+  if (*buf) w.retired.push_back(*buf);
   *buf = fresh;
   *have = need;
   return DG_OK;
@@ -202,9 +220,9 @@ dg_status get_workspace(hipStream_t stream, size_t partial_bytes, size_t counter
   if (e != hipSuccess) return fail(DG_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& w = g_ws[std::make_pair(dev, stream)];
-  dg_status st = grow(&w.partials, &w.partial_bytes, partial_bytes, 1, stream, false);
+  dg_status st = grow(w, &w.partials, &w.partial_bytes, partial_bytes, 1, stream, false);
   if (st != DG_OK) return st;
-  st = grow((void**)&w.counters, &w.counter_count, counters, sizeof(uint32_t), stream, true);
+  st = grow(w, (void**)&w.counters, &w.counter_count, counters, sizeof(uint32_t), stream, true);
   if (st != DG_OK) return st;
   *partials = (float*)w.partials;
   *counter_ptr = w.counters;
@@ -219,9 +237,9 @@ dg_status get_transpose_workspace(hipStream_t stream, size_t a_bytes, size_t b_b
   if (e != hipSuccess) return fail(DG_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& w = g_ws[std::make_pair(dev, stream)];
-  dg_status st = grow(&w.a_t, &w.a_t_bytes, a_bytes, 1, stream, false);
+  dg_status st = grow(w, &w.a_t, &w.a_t_bytes, a_bytes, 1, stream, false);
   if (st != DG_OK) return st;
-  st = grow(&w.b_t, &w.b_t_bytes, b_bytes, 1, stream, false);
+  st = grow(w, &w.b_t, &w.b_t_bytes, b_bytes, 1, stream, false);
   if (st != DG_OK) return st;
   *a = (uint8_t*)w.a_t;
   *b = (uint8_t*)w.b_t;
@@ -514,11 +532,44 @@ const char* dg_status_string(dg_status s) {
     case DG_ERR_MISALIGNED: return "DG_ERR_MISALIGNED";
     case DG_ERR_NO_DEVICE: return "DG_ERR_NO_DEVICE";
     case DG_ERR_LAUNCH: return "DG_ERR_LAUNCH";
+    case DG_ERR_CAPTURE: return "DG_ERR_CAPTURE";
   }
   return "DG_ERR_UNKNOWN";
 }
 
 const char* dg_last_error_detail(void) { return g_detail; }
+
+#ifndef DG_BUILD_ID
+#define DG_BUILD_ID "unknown"
+#endif
+const char* dg_build_id(void) { return DG_BUILD_ID; }
+
+dg_status dg_release_workspaces(void) {
+  g_detail[0] = 0;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(DG_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  std::set<int> devs;
+  for (auto& kv : g_ws) devs.insert(kv.first.first);
+  // nothing may still run on the buffers: wait for every device that holds some
+  for (int d : devs) {
+    if ((e = hipSetDevice(d)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess) {
+      (void)hipSetDevice(cur);
+      return fail(DG_ERR_LAUNCH, "synchronizing device %d: %s", d, hipGetErrorString(e));
+    }
+  }
+  for (auto& kv : g_ws) {
+    Workspace& w = kv.second;
+    (void)hipSetDevice(kv.first.first);
+    for (void* p : {w.partials, (void*)w.counters, w.a_t, w.b_t})
+      if (p) (void)hipFree(p);
+    for (void* p : w.retired) (void)hipFree(p);
+  }
+  g_ws.clear();
+  (void)hipSetDevice(cur);
+  return DG_OK;
+}
 
 }  // extern "C"
 

@@ -28,10 +28,17 @@
  *        workgroups (the M <= 64 kernels, and the last partial round of tiles of a
  *        larger dense GEMM);
  *      - transposed operand copies, for the NN / TN / TT calls.
- *    The buffers only grow and live until the process ends. Calls on one stream
- *    share them in stream order; calls on different streams never share them. A
- *    call that needs no larger buffer allocates nothing, so a call may be captured
- *    into a HIP graph once the same shape has run on that stream outside capture.
+ *    Calls on one stream share them in stream order; calls on different streams
+ *    never share them. The buffers only grow. An outgrown buffer is retired, not
+ *    freed: it stays allocated until dg_release_workspaces() or the end of the
+ *    process, so a HIP graph captured before the growth still finds its buffers.
+ *  - HIP graph capture: a call that needs no larger buffer allocates nothing, so a
+ *    call may be captured once the same shape (or a larger one) has run on that
+ *    stream outside capture. A call that would have to grow a buffer while its
+ *    stream is capturing returns DG_ERR_CAPTURE and records nothing. A graph's
+ *    launches use the capture stream's buffers: replay it on that stream, or
+ *    otherwise keep its replays ordered with eager calls on that stream (two
+ *    overlapping users of one counter set give wrong results).
  *  - A and B hold e4m3fn codes (1 byte). "NT": both are K-contiguous, B is [N][K].
  *  - C is bf16 (2 bytes), written with one round-to-nearest-even from the fp32
  *    accumulator. Only the output rows the call produces are written.
@@ -69,7 +76,9 @@ typedef enum dg_status {
   DG_ERR_UNSUPPORTED_SHAPE = 3, /* valid but beyond what the kernels index       */
   DG_ERR_MISALIGNED = 4,        /* A/B/C not 16-byte or scales not 4-byte aligned */
   DG_ERR_NO_DEVICE = 5,         /* no usable gfx950 device                       */
-  DG_ERR_LAUNCH = 6             /* the kernel launch itself failed               */
+  DG_ERR_LAUNCH = 6,            /* the kernel launch itself failed               */
+  DG_ERR_CAPTURE = 7            /* the call would allocate while its stream is    */
+                                /* being captured into a HIP graph                */
 } dg_status;
 
 /*
@@ -94,8 +103,8 @@ dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA
  * bf16 [M][N]. Same shape, alignment and error rules as dg_fp8_gemm_nt. An operand
  * that is not K-contiguous is first transposed into a library-owned buffer of the
  * stream (M*K or N*K bytes, kept and reused by later calls on that stream, released
- * only when the process ends); the results equal dg_fp8_gemm_nt's on the transposed
- * operands bit for bit.
+ * by dg_release_workspaces() or at the end of the process); the results equal
+ * dg_fp8_gemm_nt's on the transposed operands bit for bit.
  */
 dg_status dg_fp8_gemm_nn(const void* A, const void* B, void* C, const float* sfA,
                          const float* sfB, int64_t M, int64_t N, int64_t K, void* hip_stream);
@@ -225,6 +234,20 @@ typedef enum dg_dtype { DG_DTYPE_F32 = 0, DG_DTYPE_BF16 = 1 } dg_dtype;
 
 dg_status dg_quantize_fp8_1x128(const void* x, int32_t x_dtype, void* codes, float* sf,
                                 int64_t M, int64_t K, void* hip_stream);
+
+/*
+ * Frees every library-owned buffer (split-K partials and counters, transposed operand
+ * copies, retired buffers) on every device, after waiting for each such device to go
+ * idle (hipDeviceSynchronize). The caller guarantees that no library call is in
+ * flight on another thread and that no HIP graph holding a library call is replayed
+ * afterwards; later calls allocate afresh. Not callable during a stream capture.
+ * Returns DG_OK, or DG_ERR_LAUNCH if a synchronisation fails.
+ */
+dg_status dg_release_workspaces(void);
+
+/* Identifier of the sources this library was built from (a hash of the kernel
+ * sources and this header), so that a caller can tell a stale build. */
+const char* dg_build_id(void);
 
 /* Static string naming a status. */
 const char* dg_status_string(dg_status s);

@@ -102,8 +102,20 @@ def test_grouped_reject_bad_arguments(dg):
 def test_status_strings(dg):
     for code, name in enumerate(["DG_OK", "DG_ERR_NULL_POINTER", "DG_ERR_BAD_SHAPE",
                                  "DG_ERR_UNSUPPORTED_SHAPE", "DG_ERR_MISALIGNED",
-                                 "DG_ERR_NO_DEVICE", "DG_ERR_LAUNCH"]):
+                                 "DG_ERR_NO_DEVICE", "DG_ERR_LAUNCH", "DG_ERR_CAPTURE"]):
         assert status(dg, code) == name
+
+
+def test_capture_status_is_declared():
+    # a call that would allocate during a stream capture reports this status
+    text = open(HEADER).read()
+    assert re.search(r"DG_ERR_CAPTURE\s*=\s*7", text)
+
+
+def test_build_id_matches_the_sources(dg):
+    # the binding refuses a stale libdg.so; the id compiled in is the sources' hash
+    from fp8_block_scaled_dg_amd import build
+    assert dg.lib.dg_build_id().decode() == build.source_hash() == dg.BUILD_ID
 
 
 def test_config_table_is_shape_keyed(dg):

@@ -70,3 +70,65 @@ def test_graph_replays_match_eager(case):
             fn()  # an eager call on the same stream between replays
         torch.cuda.synchronize()
         assert torch.equal(c.view(torch.int16), eager.view(torch.int16)), f"{case}: eager call after replay {rep} differs"
+
+
+def test_capture_that_would_allocate_reports_capture_status():
+    """On a stream where no split-K call has run, the library would have to allocate
+    its workspace: under capture the call returns DG_ERR_CAPTURE and records nothing,
+    and the same call then runs eagerly and, once warmed, captures fine."""
+    fn, c = _dense(64, 2112, 7168, 8)
+    gu.announce("graph capture before warm-up")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    err = None
+    with torch.cuda.graph(g, stream=s):
+        try:
+            fn()
+        except dg().DGError as e:
+            err = e
+    torch.cuda.synchronize()
+    assert err is not None and err.status == 7, err
+    assert "captur" in str(err)
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.synchronize()
+    eager = c.clone()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=s):
+        fn()
+    c.zero_()
+    torch.cuda.synchronize()
+    g2.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), eager.view(torch.int16))
+
+
+def test_replay_after_workspace_growth():
+    """A graph captured on a small split-K shape keeps working after a larger shape has
+    grown the stream's workspace: the outgrown buffer is retired, not freed."""
+    small, c_small = _dense(64, 2112, 1024, 9)
+    big, c_big = _dense(64, 2112, 7168, 10)
+    gu.announce("graph replay after workspace growth")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        small()
+    torch.cuda.synchronize()
+    eager = c_small.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        small()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        big()  # grows the partials buffer of this stream
+    torch.cuda.synchronize()
+    eager_big = c_big.clone()
+    for rep in range(3):
+        c_small.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c_small.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        with torch.cuda.stream(s):
+            big()
+        torch.cuda.synchronize()
+        assert torch.equal(c_big.view(torch.int16), eager_big.view(torch.int16))
