@@ -766,14 +766,7 @@ __device__ __forceinline__ void pipe_split_tile(const PipeArgs& a, const TileVie
             v4u{__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
                 __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])},
             ws, off(part, i, j, q), 0, kSc1);
-  __builtin_amdgcn_s_waitcnt(0);  // the partial has reached memory
-  __builtin_amdgcn_s_barrier();
-  __shared__ uint32_t s_last;
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&a.counters[tt], 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(a.parts - 1);
-  __syncthreads();
-  if (!s_last) return;
+  if (!splitk_arrive(&a.counters[tt], (uint32_t)a.parts)) return;
   v16f sum[TM][TN];
   for (int pt = 0; pt < a.parts; ++pt) {
     v16f x[TM][TN];

@@ -207,15 +207,7 @@ __global__ void __launch_bounds__(Cfg::NT) skinny_kernel(SkinnyArgs args) {
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(v4u, acc[i][j]), ws,
             split * per_split + (((wave * TM + i) * TN + j) * 64 + lane) * 16, 0, kSc1);
-    __builtin_amdgcn_s_waitcnt(0);  // every partial store (and stray load) has completed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    __shared__ uint32_t s_last;
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(&args.counters[tile], 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(S - 1);
-    __syncthreads();
-    if (!s_last) return;
+    if (!splitk_arrive(&args.counters[tile], (uint32_t)S)) return;
     v4u part[SMAX][TM][TN];
 #pragma unroll
     for (int sp = 0; sp < SMAX; ++sp) {

@@ -233,8 +233,8 @@ __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
   stream_compute<Cfg, 0, PACKED>(acc, r, ks, g, l16, kb0 & 3);
 
   // ---- split reduction. Partials are written and read with device-scope (sc1)
-  // 16-byte accesses (measured faster here than L2-resident ones); waiting for every
-  // store before the arrival count is taken makes the count a release.
+  // 16-byte accesses (measured faster here than L2-resident ones); splitk_arrive
+  // orders them around the arrival count.
   if (S > 1) {
     constexpr int SMAX = Cfg::SMAX;
     constexpr int per_split = 64 * BN * 4;
@@ -248,14 +248,7 @@ __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(v4u, acc[i][j]), ws,
             split * per_split + (((wave * TM + i) * TN + j) * 64 + lane) * 16, 0, kSc1);
-    __builtin_amdgcn_s_waitcnt(0);  // the partial has reached memory
-    __builtin_amdgcn_s_barrier();
-    __shared__ uint32_t s_last;
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(&args.counters[tile], 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(S - 1);
-    __syncthreads();
-    if (!s_last) return;
+    if (!splitk_arrive(&args.counters[tile], (uint32_t)S)) return;
     // the other splits' partials (this split's is in registers)
     v4u part[SMAX][TM][TN];
 #pragma unroll
