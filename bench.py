@@ -40,7 +40,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
-ROTATE_BYTES = 512 * 1024 * 1024
+MAX_COPIES = 64  # rotation sets per GEMM: enough to defeat L2 and MALL, few enough to set up
+PEAK_CLOCK_GHZ = 2.4  # the clock the published FP8 peak is quoted at
+DECODE_BYTES = {"dec2112": 15886048, "dec32768": 21009408}
 METRIC = "FP8 block-scaled GEMM TFLOPS (%MFMA peak) and GB/s at M=64 (%HBM), 1 MI355X"
 
 WORKLOADS = {
@@ -330,6 +332,139 @@ def oracle_leg(gemms, last_set: int, sfa_layout: str = "f32", budget_macs: float
     return per_step, "; ".join(samples), checks
 
 
+class ClockSampler:
+    """Samples the GPU's current shader (gfx) clock through amdsmi in a background
+    thread while a timed region runs; mean() is the average over the samples (MHz),
+    or None where amdsmi reports nothing."""
+
+    def __init__(self, period_s: float = 0.002):
+        import threading
+        self.period, self.samples, self._stop = period_s, [], threading.Event()
+        self._thread, self.handle = None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self.amdsmi, self.handle = amdsmi, (handles[0] if handles else None)
+        except Exception:  # no amdsmi, or no access: the clock stays unreported
+            self.handle = None
+
+    def _read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        xs = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and x > 0]
+        if xs:
+            return sum(xs) / len(xs)
+        x = m.get("current_gfxclk")
+        return float(x) if isinstance(x, (int, float)) and x > 0 else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except Exception:
+                return
+            if v:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self.handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def mean(self):
+        return sum(self.samples) / len(self.samples) if self.samples else None
+
+
+def timed_launches(launch, K: int, start: int, graph: bool, sampler=None):
+    """Average duration (ms) of K back-to-back launches launch(start), ..., launch(start
+    + K - 1), between two HIP events on the stream the launches run on. graph: the K
+    launches are first captured into one HIP graph on a side stream (after a warm call
+    there, so that the library's per-stream buffers exist) and the replay is timed:
+    the GPU then runs them back to back without host launch gaps."""
+    import torch
+    s = torch.cuda.Stream() if graph else torch.cuda.current_stream()
+    g = None
+    if graph:
+        with torch.cuda.stream(s):
+            launch(start)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(K):
+                launch(start + i)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):  # one untimed replay
+            g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ctx = sampler if sampler is not None else _Null()
+    with torch.cuda.stream(s), ctx:
+        e0.record(s)
+        if graph:
+            g.replay()
+        else:
+            for i in range(K):
+                launch(start + i)
+        e1.record(s)
+        e1.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+def hbm_ceiling(nbytes_list, rotate_bytes: int, reps: int = 50):
+    """The streaming-read probe (libdg_probe.so) on each byte count, rotated over
+    rotate_bytes of buffers, graph-timed: the best over grid sizes and load kinds of
+    the average per-launch time, and the empty-kernel time."""
+    import ctypes
+    import torch
+    from fp8_block_scaled_dg_amd import build as dgb
+    lib = ctypes.CDLL(dgb.PROBE_LIB_PATH)
+    lib.dg_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.dg_probe_empty.argtypes = [ctypes.c_void_p]
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda:0")
+    out = {}
+    for nb in nbytes_list:
+        nb16 = nb // 16 * 16
+        copies = max(1, min(64, -(-rotate_bytes // nb16)))
+        bufs = [torch.empty(nb16, dtype=torch.uint8, device="cuda:0").fill_(i % 251)
+                for i in range(copies)]
+        best = None
+        for blocks in (256, 512, 1024, 2048):
+            for nt in (0, 1):
+                def launch(i, blocks=blocks, nt=nt):
+                    st = torch.cuda.current_stream().cuda_stream
+                    rc = lib.dg_probe_stream_read(bufs[i % copies].data_ptr(), nb16,
+                                                  sink.data_ptr(), blocks, nt, st)
+                    assert rc == 0, rc
+                ms = timed_launches(launch, reps, 0, graph=True)
+                if best is None or ms < best[0]:
+                    best = (ms, blocks, nt)
+        out[str(nb)] = dict(bytes=nb16, us=best[0] * 1e3, gbs=nb16 / (best[0] * 1e-3) / 1e9,
+                            blocks=best[1], nontemporal=bool(best[2]))
+        del bufs
+
+    def empty(i):
+        assert lib.dg_probe_empty(torch.cuda.current_stream().cuda_stream) == 0
+    out["empty_kernel_us"] = timed_launches(empty, reps, 0, graph=True) * 1e3
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,8 +472,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--warmup-seconds", type=float, default=0.5,
                     help="keep running untimed warmup steps past --warmup until this much "
-                         "time has passed, so that the GPU clocks have left their idle state")
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+                         "time has passed, so that the GPU clocks have left their idle state "
+                         "(0: exactly --warmup steps, e.g. under a profiler)")
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS) + ["hbm_ceiling"])
+    ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
+                    help="graph: the K launches of each GEMM are captured into a HIP graph "
+                         "and replayed (no host launch gaps); eager: launched from Python")
+    ap.add_argument("--rotate-mb", type=int, default=512,
+                    help="input/output sets rotate over this many MB (0: one set); at most "
+                         f"{MAX_COPIES} copies")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the compute-bound prefill leg of the default decode run")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling of the default decode run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", choices=("nt", "nn", "tn", "tt"), default="nt",
                     help="memory layout of the dense GEMMs' operands (A [K][M] for t, "
@@ -370,9 +516,18 @@ def main():
         copy_calibration()
         return
     import synth
-    import fp8_block_scaled_dg_amd as dg  # noqa: F401  (fails loudly if libdg.so is missing)
+    import fp8_block_scaled_dg_amd as dg  # fails loudly if libdg.so is missing or stale
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    rotate = args.rotate_mb * 1024 * 1024
+    if args.workload == "hbm_ceiling":
+        ceil = hbm_ceiling([DECODE_BYTES["dec2112"], DECODE_BYTES["dec32768"]], rotate)
+        print(json.dumps({"metric": "streaming-read GB/s at the decode GEMMs' byte counts",
+                          "value": ceil[str(DECODE_BYTES["dec2112"])]["gbs"], "unit": "GB/s",
+                          "n_gpus": 1, "higher_is_better": True, "data": "synthetic",
+                          "config": {"workload": "plain streaming read (libdg_probe.so)"},
+                          "hbm_ceiling": ceil}), flush=True)
+        return
     names = WORKLOADS[args.workload]
     if args.gemm is not None:
         if args.gemm not in names:
@@ -383,7 +538,7 @@ def main():
              Gemm(n, synth.workload(n), args.sfa, args.layout)
              for n in names]
     step_footprint = sum(g.footprint for g in gemms)
-    copies = max(1, -(-ROTATE_BYTES // step_footprint))
+    copies = max(1, min(MAX_COPIES, -(-rotate // step_footprint)))
     for g in gemms:
         g.upload(copies, args.sfa)
     torch.cuda.synchronize()
@@ -397,35 +552,29 @@ def main():
                 g.launch(s)
         warm += chunk
         torch.cuda.synchronize()
-    args.warmup = warm  # the number of untimed steps actually run
+    warmup_run = warm  # the number of untimed steps actually run
 
     # Timed region: the K steps' launches, grouped by GEMM (all K launches of one GEMM
-    # back to back on rotating buffers, then the next GEMM), bracketed by events on
-    # the launch stream: a group's elapsed time / K is that kernel's average launch
-    # duration (kernel time plus the back-to-back dispatch gap), and the total over
-    # all groups / K is the time of one step of the whole path.
+    # back to back on rotating buffers, then the next GEMM), each group bracketed by
+    # events on its launch stream: a group's elapsed time / K is that kernel's average
+    # launch duration, and the sum over the groups is the time of one step. With graph
+    # timing a group is one replayed HIP graph of its K launches; the eager figures
+    # (launches from Python, host launch gaps included) are reported beside it.
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in gemms]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    graph = args.timing == "graph"
     wall0 = time.perf_counter()
-    start.record()
-    for j, g in enumerate(gemms):
-        ev[j][0].record()
-        for s in range(K):
-            g.launch(args.warmup + s)
-        ev[j][1].record()
-    end.record()
-    torch.cuda.synchronize()
+    per_ms = [timed_launches(g.launch, K, warmup_run, graph) for g in gemms]
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
+    eager_ms = per_ms if not graph else [timed_launches(g.launch, K, warmup_run, False)
+                                         for g in gemms]
+    ms_per_step = sum(per_ms)
+    last_set = warmup_run + K - 1
 
     kern = []
     for j, g in enumerate(gemms):
-        ms = ev[j][0].elapsed_time(ev[j][1]) / K
+        ms = per_ms[j]
         kern.append(dict(name=g.name, shape=g.shape, avg_us=ms * 1e3,
+                         eager_avg_us=eager_ms[j] * 1e3,
                          tflops=g.flops / (ms * 1e-3) / 1e12,
                          gbs=g.bytes / (ms * 1e-3) / 1e9,
                          alg_bytes=g.bytes, alg_flops=g.flops))
@@ -439,29 +588,36 @@ def main():
 
     dom = max(range(len(gemms)), key=lambda j: kern[j]["avg_us"])
     kd = kern[dom]
-    if memory_bound:
+    t_mem = kd["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = kd["alg_flops"] / (FP8_PEAK_TFLOPS * 1e12)
+    if memory_bound or t_mem > t_mfma:
         roof = dict(bound="hbm", achieved=kd["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=kd["gbs"] / HBM_PEAK_GBS)
     else:
-        t_mem = kd["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
-        t_mfma = kd["alg_flops"] / (FP8_PEAK_TFLOPS * 1e12)
-        if t_mfma >= t_mem:
-            roof = dict(bound="mfma", achieved=kd["tflops"], peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=kd["tflops"] / FP8_PEAK_TFLOPS)
-        else:
-            roof = dict(bound="hbm", achieved=kd["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=kd["gbs"] / HBM_PEAK_GBS)
+        roof = dict(bound="mfma", achieved=kd["tflops"], peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=kd["tflops"] / FP8_PEAK_TFLOPS)
     roof["kernel"] = kd["name"]
-    roof["traffic"] = measured_traffic(kd["name"])
+    roof["traffic"] = measured_traffic(kd["name"], dg.BUILD_ID)
+
+    line_extra = {}
+    if args.workload == "decode" and not args.no_ceiling and args.gemm is None:
+        ceil = hbm_ceiling([g.bytes for g in gemms], rotate)
+        line_extra["hbm_ceiling"] = ceil
+        c = ceil[str(kd["alg_bytes"])]
+        roof["ceiling_gbs"] = c["gbs"]
+        roof["frac_of_ceiling"] = kd["gbs"] / c["gbs"]
+    if args.workload == "decode" and not args.no_prefill and args.gemm is None:
+        line_extra.update(prefill_leg(max(K, 50), rotate, graph))
+        line_extra["roofline_mfma"] = line_extra["prefill"].pop("roofline")
 
     cpu = None
     if not args.no_cpu_baseline:
         if args.workload == "quant":
-            per_step, sample, checks = quant_oracle_leg(gemms[0], args.warmup + K - 1)
+            per_step, sample, checks = quant_oracle_leg(gemms[0], last_set)
         elif args.workload == "moe_swiglu":
-            per_step, sample, checks = swiglu_oracle_leg(gemms[0], args.warmup + K - 1)
+            per_step, sample, checks = swiglu_oracle_leg(gemms[0], last_set)
         else:
-            per_step, sample, checks = oracle_leg(gemms, args.warmup + K - 1, args.sfa)
+            per_step, sample, checks = oracle_leg(gemms, last_set, args.sfa)
         import oracle
         cores = oracle.num_threads()
         cpu_value = (step_bytes / per_step / 1e9) if memory_bound else (step_flops / per_step / 1e12)
@@ -475,8 +631,10 @@ def main():
         "unit": unit,
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup_run,
+        "warmup_requested": args.warmup,
         "ms_per_step": ms_per_step,
+        "eager_ms_per_step": sum(eager_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -484,7 +642,7 @@ def main():
         "data": "synthetic",
         "config": ({"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) rounded "
                     "to bf16", "output": "e4m3fn codes + fp32 power-of-two scale per 1x128",
-                    "parallelism": "single GPU", "rotation_copies": copies}
+                    "parallelism": "single GPU", "rotation_copies": copies, "timing": args.timing}
                    if args.workload == "quant" else
                    {"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) quantized to "
                     "e4m3fn, A per 1x128, B per 128x128, power-of-two scales",
@@ -494,14 +652,66 @@ def main():
                     "output": ("e4m3fn codes + fp32 scale per 1x128 of silu(gate) * up"
                                if args.workload == "moe_swiglu" else "bf16"),
                     "parallelism": "single GPU",
-                    "rotation_copies": copies}),
+                    "rotation_copies": copies,
+                    "timing": args.timing}),
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kern,
+        **line_extra,
         "wall_s": wall,
-        "kernel_source": kernel_source_hash(),
+        "build_id": dg.BUILD_ID,
     }
     print(json.dumps(line), flush=True)
+
+
+def prefill_leg(K: int, rotate: int, graph: bool) -> dict:
+    """The compute-bound half of the metric: the dense prefill GEMM 4096x7168x18432,
+    K launches timed like the step's GEMMs, against the dense FP8 MFMA peak; the shader
+    clock sampled during the timed launches gives the peak at the clock the chip ran.
+    The last launch's output is checked against the oracle on seeded whole rows."""
+    import numpy as np
+    import torch
+    import synth
+    g = Gemm("prefill", synth.workload("prefill"))
+    copies = max(1, min(MAX_COPIES, -(-rotate // g.footprint)))
+    g.upload(copies)
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < 0.5 or i < 20:
+        g.launch(i)
+        i += 1
+        if i % 20 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    sampler = ClockSampler()
+    ms = timed_launches(g.launch, K, i, graph, sampler)
+    tflops = g.flops / (ms * 1e-3) / 1e12
+    mhz = sampler.mean()
+    roof = dict(bound="mfma", achieved=tflops, peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=tflops / FP8_PEAK_TFLOPS, kernel="prefill",
+                clock_ghz=(mhz / 1e3) if mhz else None,
+                peak_at_clock=(FP8_PEAK_TFLOPS * mhz / 1e3 / PEAK_CLOCK_GHZ) if mhz else None,
+                frac_at_clock=(tflops / (FP8_PEAK_TFLOPS * mhz / 1e3 / PEAK_CLOCK_GHZ))
+                if mhz else None,
+                clock_samples=len(sampler.samples))
+    # parity of the last timed launch on seeded whole rows
+    import oracle
+    from tests.parity import report
+    w = g.w
+    rows = np.sort(np.random.default_rng(4321).choice(w.shape[0], 32, replace=False))
+    N = w.shape[1]
+    ri = np.repeat(rows, N).astype(np.int64)
+    ni = np.tile(np.arange(N, dtype=np.int64), rows.size)
+    r = oracle.gemm_nt_at(w.A, w.B, w.sfA, w.sfB, ri, ni)
+    C = g.sets[(i + K - 1) % len(g.sets)]["C"].view(torch.int16).cpu().numpy().view(np.uint16)
+    rep = report(C[ri, ni], r)
+    out = dict(shape=g.shape, launches=K, avg_us=ms * 1e3, tflops=tflops, alg_flops=g.flops,
+               alg_bytes=g.bytes, rotation_copies=copies,
+               parity={k: rep[k] for k in ("n", "max_excess_rel", "bitwise_match", "n_fail", "nan")},
+               roofline=roof)
+    del g
+    torch.cuda.empty_cache()
+    return {"prefill": out}
 
 
 def copy_calibration(nbytes: int = 256 * 1024 * 1024, reps: int = 5):
@@ -516,16 +726,16 @@ def copy_calibration(nbytes: int = 256 * 1024 * 1024, reps: int = 5):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def measured_traffic(kernel_name: str):
+def measured_traffic(kernel_name: str, build_id: str):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, if it was taken on the current kernel sources; else None."""
+    summary, if it was taken on the library build now loaded; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source") != kernel_source_hash():
+    if rec.get("build_id") != build_id:
         return None
     return rec.get("bytes_per_launch", {}).get(kernel_name)
 
