@@ -73,6 +73,8 @@ lib.dg_last_error_detail.argtypes = []
 lib.dg_describe_config.restype = ctypes.c_int
 lib.dg_describe_config.argtypes = [_i32, _i64, _i64, _i64, _i32, _i64, ctypes.c_char_p, _i64]
 
+lib.dg_fp8_gemm_nt_noalloc.restype = ctypes.c_int
+lib.dg_fp8_gemm_nt_noalloc.argtypes = lib.dg_fp8_gemm_nt.argtypes
 lib.dg_fp8_gemm_nt_ue8m0.restype = ctypes.c_int
 lib.dg_fp8_gemm_nt_ue8m0.argtypes = lib.dg_fp8_gemm_nt.argtypes
 lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.restype = ctypes.c_int

@@ -213,8 +213,57 @@ dg_status grow(Workspace& w, void** buf, size_t* have, size_t need, size_t elem,
   return DG_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free scratch
+//
+// dg_fp8_gemm_nt_noalloc runs the dense GEMM without any allocation: the split-K
+// partials and arrival counters live in this fixed array, one copy per GPU the
+// library runs on (zero-filled when the code object is loaded, held until the
+// process ends). Host code never passes `scratch` itself to a kernel -- on the host
+// it only names the symbol -- but the device address hipGetSymbolAddress gives for
+// the current device, looked up once per device. Every allocation-free call on a GPU
+// shares its array: the counters are zero between calls because each kernel resets
+// the ones it used, and two such calls that overlap on one GPU race.
+constexpr size_t kScratchPartialBytes = size_t(32) << 20;  // fp32 partial tiles
+constexpr size_t kScratchCounters = 4096;                   // per-tile arrival counters
+static __device__ __align__(256) uint8_t
+    scratch[kScratchPartialBytes + kScratchCounters * sizeof(uint32_t)];
+
+thread_local bool g_noalloc = false;  // set for the duration of an allocation-free call
+std::mutex g_scratch_mu;
+std::map<int, uint8_t*> g_scratch_ptr;  // device -> device address of its `scratch`
+
+struct NoAllocCall {
+  NoAllocCall() { g_noalloc = true; }
+  ~NoAllocCall() { g_noalloc = false; }
+};
+
+dg_status scratch_workspace(size_t partial_bytes, size_t counters, float** partials,
+                            uint32_t** counter_ptr) {
+  if (partial_bytes > kScratchPartialBytes || counters > kScratchCounters)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE,
+                "this shape needs %zu bytes of split-K partials and %zu counters; the "
+                "allocation-free call holds at most %zu bytes and %zu counters",
+                partial_bytes, counters, kScratchPartialBytes, kScratchCounters);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DG_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    uint8_t* ptr = nullptr;
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DG_ERR_LAUNCH, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *partials = (float*)it->second;
+  *counter_ptr = (uint32_t*)(it->second + kScratchPartialBytes);
+  return DG_OK;
+}
+
 dg_status get_workspace(hipStream_t stream, size_t partial_bytes, size_t counters,
                         float** partials, uint32_t** counter_ptr) {
+  if (g_noalloc) return scratch_workspace(partial_bytes, counters, partials, counter_ptr);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(DG_ERR_NO_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
@@ -665,6 +714,13 @@ extern "C" {
 
 dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA,
                          const float* sfB, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_dense(A, B, C, sfA, 0, sfB, M, N, K, stream);
+}
+
+dg_status dg_fp8_gemm_nt_noalloc(const void* A, const void* B, void* C, const float* sfA,
+                                 const float* sfB, int64_t M, int64_t N, int64_t K,
+                                 void* stream) {
+  NoAllocCall scope;
   return gemm_dense(A, B, C, sfA, 0, sfB, M, N, K, stream);
 }
 

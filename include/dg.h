@@ -92,6 +92,23 @@ dg_status dg_fp8_gemm_nt(const void* A, const void* B, void* C, const float* sfA
                          void* hip_stream);
 
 /*
+ * dg_fp8_gemm_nt without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture (also before the shape has run eagerly),
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, results and
+ * errors as dg_fp8_gemm_nt (bitwise the same output); the call allocates nothing and
+ * records no memset. The split-K partials and arrival counters it needs live in one
+ * fixed device array per GPU, part of the library's code object and held until the
+ * process ends: at most 32 MiB of partials and 4096 counters, which covers every
+ * shape the configuration table serves (a shape needing more returns
+ * DG_ERR_UNSUPPORTED_SHAPE). Every call on a GPU shares that GPU's array and leaves
+ * its counters at zero; calls that overlap in time on one GPU (on different streams,
+ * or graph replays concurrent with eager calls) race and give wrong results.
+ */
+dg_status dg_fp8_gemm_nt_noalloc(const void* A, const void* B, void* C, const float* sfA,
+                                 const float* sfB, int64_t M, int64_t N, int64_t K,
+                                 void* hip_stream);
+
+/*
  * The same dense GEMM in the other memory layouts of one GEMM family (project page,
  * "core features": NT / TN / NN / TT layouts, for forward, backward and inference):
  * C = op(A) op(B) with op = N (as stored) or T (transposed), i.e.
