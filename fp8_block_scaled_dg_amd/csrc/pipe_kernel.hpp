@@ -284,12 +284,13 @@ struct PipeScales {
 // B tile 1 of kb+1 are read (B tile 1 into spare registers). B tile 0 of kb+1 is
 // read after M7, when kb's is dead. Scheduling fences keep this order; the compiler
 // inserts only the LDS waits.
-template <class Cfg, int S, bool ACT>
+template <class Cfg, int S, int MODE>
 __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeLane<Cfg>& pl,
                                           v16f (&acc)[2][2], Frag0& f, v16f (&carry)[2],
                                           float& carry_s, PipeScales& sc, int kb, int KB,
                                           int wave) {
-  if constexpr (!ACT) {
+  constexpr bool HI = MODE == 2;  // the wave's second 32-row A tile holds output rows
+  if constexpr (MODE == 0) {
     // a wave with no output rows or columns of its own: only its share of the DMAs
     wait_vm_lgkm0<Cfg::OPS_PER_KB>();
     __builtin_amdgcn_s_barrier();
@@ -303,7 +304,7 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   const v16f zero = {};
 
   v8i a10, a11;
-  read_tile(st, pl.va, 1, a10, a11);
+  if (HI) read_tile(st, pl.va, 1, a10, a11);
   if (S == 0) {
     // scales of K-blocks kb..kb+2 (landed before the previous barrier): three fp32
     // values, or (packed) bytes kb % 4 .. kb % 4 + 2 of the words from kb / 4 on
@@ -333,16 +334,16 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   }
   DG_FENCE();
   v16f p00 = mfma32(f.b0, f.a0, zero);  // M1
-  promote8<0>(acc[1][0], carry[0], carry_s);
+  if (HI) promote8<0>(acc[1][0], carry[0], carry_s);
   DG_FENCE();
   v16f p01 = mfma32(f.c0, f.a0, zero);  // M2
-  promote8<8>(acc[1][0], carry[0], carry_s);
+  if (HI) promote8<8>(acc[1][0], carry[0], carry_s);
   DG_FENCE();
   p00 = mfma32(f.b1, f.a1, p00);  // M3
-  promote8<0>(acc[1][1], carry[1], carry_s);
+  if (HI) promote8<0>(acc[1][1], carry[1], carry_s);
   DG_FENCE();
   p01 = mfma32(f.c1, f.a1, p01);  // M4
-  promote8<8>(acc[1][1], carry[1], carry_s);
+  if (HI) promote8<8>(acc[1][1], carry[1], carry_s);
   DG_FENCE();
   // block kb+1 in LDS, block kb's stage free. Block kb+3's DMAs into it are spread
   // over M5..M8, a quarter behind each (instead of all eight waves queueing a whole
@@ -357,42 +358,47 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   const float s0 = sc.s0[S], s1 = sc.s1[S];
   read_tile(nst, pl.va, 0, f.a0, f.a1);
   DG_FENCE();
-  v16f p10 = mfma32(f.b0, a10, zero);  // M5
+  v16f p10, p11;
+  if (HI) p10 = mfma32(f.b0, a10, zero);  // M5
   pipe_issue_ops<Cfg, S, S == 0, 0, Q1>(th, kn, wave);
   v8i c0n, c1n;
   read_tile(nst, pl.vb, 1, c0n, c1n);
   promote8<0>(acc[0][0], p00, s0);
   DG_FENCE();
-  v16f p11 = mfma32(f.c0, a10, zero);  // M6
+  if (HI) p11 = mfma32(f.c0, a10, zero);  // M6
   pipe_issue_ops<Cfg, S, false, Q1, Q2>(th, kn, wave);
   promote8<8>(acc[0][0], p00, s0);
   DG_FENCE();
-  p10 = mfma32(f.b1, a11, p10);  // M7
+  if (HI) p10 = mfma32(f.b1, a11, p10);  // M7
   pipe_issue_ops<Cfg, S, false, Q2, Q3>(th, kn, wave);
   promote8<0>(acc[0][1], p01, s0);
   DG_FENCE();
   read_tile(nst, pl.vb, 0, f.b0, f.b1);
   DG_FENCE();
-  p11 = mfma32(f.c1, a11, p11);  // M8
+  if (HI) p11 = mfma32(f.c1, a11, p11);  // M8
   pipe_issue_ops<Cfg, S, false, Q3, OPS>(th, kn, wave);
   promote8<8>(acc[0][1], p01, s0);
   DG_FENCE();
   f.c0 = c0n;
   f.c1 = c1n;
-  carry[0] = p10;
-  carry[1] = p11;
+  if (HI) {
+    carry[0] = p10;
+    carry[1] = p11;
+  }
   carry_s = s1;
 }
 
 // Multiplies rows [m0, m0+BM) of the view by columns [n0, n0+BN) over the K-blocks
 // [kb_lo, kb_hi) and leaves the fp32 tile in acc (lane layout: row lane % 32 of each
 // 32x32 tile, columns 8*(e/4) + 4*(lane/32) + e%4). Rows at or past v.rows and
-// columns at or past N read as zero (the buffer resources end there). With ACT false
-// the wave only moves its share of the tile's operands and leaves acc at zero: the
-// caller passes false to a wave whose 64 x 64 sub-tile holds nothing to store.
+// columns at or past N read as zero (the buffer resources end there). MODE 0: the wave
+// only moves its share of the tile's operands and leaves acc at zero (its 64 x 64
+// sub-tile holds nothing to store); MODE 1: only the sub-tile's first 32 rows hold
+// output, and the MFMAs and promotion of its second 32-row A tile are skipped (acc[1]
+// stays zero); MODE 2: the whole sub-tile.
 // b_hi: tile rows from 128 on come from B rows b_hi further on (and their sfB blocks
 // likewise): the up half of a [gate; up] B, b_hi = I - 128. 0 for a plain tile.
-template <class Cfg, bool ACT>
+template <class Cfg, int MODE>
 __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileView& v, int kb_lo,
                                                  int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN],
                                                  int b_hi) {
@@ -459,7 +465,7 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
   DG_FENCE();
   pipe_issue<Cfg, 2, false>(th, kb_lo + 2 < kb_hi ? kb_lo + 2 : kb_hi - 1, wave);
   DG_FENCE();
-  if (ACT) {
+  if (MODE > 0) {
     read_tile(read_base<0>(), pl.va, 0, f.a0, f.a1);
     read_tile(read_base<0>(), pl.vb, 0, f.b0, f.b1);
     read_tile(read_base<0>(), pl.vb, 1, f.c0, f.c1);
@@ -467,14 +473,14 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
   DG_FENCE();
   int kb = kb_lo;
   for (; kb + 3 <= kb_hi; kb += 3) {
-    pipe_step<Cfg, 0, ACT>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
-    pipe_step<Cfg, 1, ACT>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
-    pipe_step<Cfg, 2, ACT>(th, pl, acc, f, carry, carry_s, sc, kb + 2, kb_hi, wave);
+    pipe_step<Cfg, 0, MODE>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
+    pipe_step<Cfg, 1, MODE>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
+    pipe_step<Cfg, 2, MODE>(th, pl, acc, f, carry, carry_s, sc, kb + 2, kb_hi, wave);
   }
-  if (kb < kb_hi) pipe_step<Cfg, 0, ACT>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
+  if (kb < kb_hi) pipe_step<Cfg, 0, MODE>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
   if (kb + 1 < kb_hi)
-    pipe_step<Cfg, 1, ACT>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
-  if (ACT) {
+    pipe_step<Cfg, 1, MODE>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
+  if (MODE == 2) {
     promote8<0>(acc[1][0], carry[0], carry_s);
     promote8<8>(acc[1][0], carry[0], carry_s);
     promote8<0>(acc[1][1], carry[1], carry_s);
@@ -487,20 +493,25 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
   DG_FENCE();
 }
 
-// The wave's sub-tile holds output when its first row is below v.rows and its first
-// column below N; `any_row` lets the caller rule out sub-tiles whose rows are all
-// someone else's (contiguous layout). Both branches pass the same barriers.
+// Which 32-row halves of the wave's sub-tile hold output: a half does when its first
+// row is below v.rows and the sub-tile's first column below N; `quarters` (bit q for
+// the tile's 32-row quarter q) lets the caller rule out quarters whose rows are all
+// someone else's (contiguous layout). The three modes pass the same barriers.
 template <class Cfg>
 __device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& v, int kb_lo,
                                               int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN],
-                                              bool any_row = true, int b_hi = 0) {
+                                              uint32_t quarters = ~0u, int b_hi = 0) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
-  const bool act = any_row && v.m0 + wm * 64 < v.rows && v.n0 + wn * 64 < p.N;
-  if (act)
-    pipe_mainloop_as<Cfg, true>(p, v, kb_lo, kb_hi, acc, b_hi);
+  const bool cols = v.n0 + wn * 64 < p.N;
+  const bool lo = cols && ((quarters >> (2 * wm)) & 1) && v.m0 + wm * 64 < v.rows;
+  const bool hi = cols && ((quarters >> (2 * wm + 1)) & 1) && v.m0 + wm * 64 + 32 < v.rows;
+  if (hi)
+    pipe_mainloop_as<Cfg, 2>(p, v, kb_lo, kb_hi, acc, b_hi);
+  else if (lo)
+    pipe_mainloop_as<Cfg, 1>(p, v, kb_lo, kb_hi, acc, b_hi);
   else
-    pipe_mainloop_as<Cfg, false>(p, v, kb_lo, kb_hi, acc, b_hi);
+    pipe_mainloop_as<Cfg, 0>(p, v, kb_lo, kb_hi, acc, b_hi);
 }
 
 // bf16 RNE store of a finished tile: produced rows (< valid_rows, and for the
@@ -661,14 +672,14 @@ __device__ __forceinline__ void pipe_store_swiglu(const Problem& p, const TileVi
 
 template <class Cfg, int KIND, bool SWIGLU = false>
 __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, int expert,
-                                          int valid_rows, bool any_row = true,
+                                          int valid_rows, uint32_t quarters = ~0u,
                                           SwigluOut sw = SwigluOut{}) {
   v16f acc[Cfg::TM][Cfg::TN];
   if constexpr (SWIGLU) {
-    pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, any_row, sw.I - 128);
+    pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, quarters, sw.I - 128);
     pipe_store_swiglu<Cfg, KIND>(p, v, expert, valid_rows, acc, sw);
   } else {
-    pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, any_row);
+    pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, quarters);
     pipe_store<Cfg, KIND>(p, v, expert, valid_rows, acc);
   }
 }
@@ -856,7 +867,7 @@ __device__ __forceinline__ void pipe_item(const PipeArgs& args, int item) {
     SwigluOut sw = args.sw;  // this expert's rows of the fused epilogue's outputs
     sw.codes += (int64_t)e * p.M * sw.I;
     sw.sf += (int64_t)e * p.M * (sw.I / 128);
-    pipe_tile<Cfg, KIND, SWIGLU>(p, v, e, valid, true, sw);
+    pipe_tile<Cfg, KIND, SWIGLU>(p, v, e, valid, ~0u, sw);
     return;
   }
   const int t = xcd_tile_order(item, KIND == kDense ? args.full_tiles : args.items);
@@ -874,12 +885,12 @@ __device__ __forceinline__ void pipe_item(const PipeArgs& args, int item) {
     return;
   }
   // contiguous: one pass per distinct expert id among the tile's rows, in
-  // increasing id order (one pass when segments are BM-aligned). s_half[h] records
-  // that 64-row half h holds a row of the current expert; a wave whose half holds
-  // none (padding, or another expert's rows) only moves operands.
+  // increasing id order (one pass when segments are BM-aligned). s_quarter[q] records
+  // that 32-row quarter q holds a row of the current expert; a wave skips the MFMAs
+  // of a quarter that holds none (padding, or another expert's rows).
   __shared__ int s_next;
-  __shared__ int s_half[Cfg::BM / 64];
-  if (threadIdx.x < Cfg::BM / 64) s_half[threadIdx.x] = -1;
+  __shared__ int s_quarter[Cfg::BM / 32];
+  if (threadIdx.x < Cfg::BM / 32) s_quarter[threadIdx.x] = -1;
   int id = -1;
   if (threadIdx.x < Cfg::BM) {
     const int64_t row = v.m0 + threadIdx.x;
@@ -892,14 +903,16 @@ __device__ __forceinline__ void pipe_item(const PipeArgs& args, int item) {
     if (id > prev && id < p.G) atomicMin(&s_next, id);
     __syncthreads();
     const int e = __builtin_amdgcn_readfirstlane(s_next);
-    if (id == e) s_half[threadIdx.x >> 6] = e;
+    if (id == e) s_quarter[threadIdx.x >> 5] = e;
     __syncthreads();
     if (e == 0x7FFFFFFF) break;
-    const int wm = (int)(threadIdx.x >> 6) / Cfg::WAVES_N;
-    const bool any_row = __builtin_amdgcn_readfirstlane(s_half[wm]) == e;
+    uint32_t quarters = 0;
+#pragma unroll
+    for (int q = 0; q < Cfg::BM / 32; ++q)
+      quarters |= (uint32_t)(__builtin_amdgcn_readfirstlane(s_quarter[q]) == e) << q;
     v.B = p.B + (int64_t)e * p.N * p.K;
     v.sfB = p.sfB + (int64_t)e * NB * KB;
-    pipe_tile<Cfg, KIND, SWIGLU>(p, v, e, (int)p.M, any_row, args.sw);
+    pipe_tile<Cfg, KIND, SWIGLU>(p, v, e, (int)p.M, quarters, args.sw);
     prev = e;
   }
 }

@@ -292,6 +292,40 @@ def test_masked_integer_exact_bitwise():
         assert_bitwise(g[produced], r[produced], "masked int")
 
 
+def test_masked_32_row_boundaries_bitwise():
+    # valid-row counts on both sides of every 32-row boundary of a 128-row tile: the
+    # wave whose 64-row half holds 1..32 rows skips its second 32-row A tile
+    rng = np.random.default_rng(57)
+    masked_m = np.array([1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 160, 192, 200],
+                        dtype=np.int32)
+    G, M_max, N, K = masked_m.size, 256, 384, 512
+    A, B, sfA, sfB = int_operands(rng, G * M_max, N, K, G=G)
+    A, sfA = A.reshape(G, M_max, K), sfA.reshape(G, M_max, K // 128)
+    for e in range(G):
+        A[e, masked_m[e]:] = synth.FP8_NAN_CODE  # never read into an output
+    g, init = run_masked(A, B, sfA, sfB, masked_m)
+    r, produced = oracle.grouped_masked(A, B, sfA, sfB, masked_m)
+    assert np.array_equal(g[~produced], init[~produced]), "masked rows touched"
+    assert_bitwise(g[produced], r[produced], "masked 32-row boundaries")
+
+
+def test_contiguous_32_row_boundaries_bitwise():
+    # segment lengths ending on both sides of 32-row boundaries (pad rows fill each
+    # segment to a multiple of 128)
+    rng = np.random.default_rng(58)
+    counts = np.array([1, 31, 32, 33, 64, 65, 96, 97, 127, 160], dtype=np.int32)
+    G, N, K = counts.size, 272, 384
+    m_indices = synth.contiguous_layout(counts)
+    A, B, sfA, sfB = int_operands(rng, m_indices.size, N, K, G=G)
+    A[m_indices < 0] = synth.FP8_NAN_CODE
+
+    class W: pass
+    w = W()
+    w.A, w.B, w.sfA, w.sfB, w.m_indices = A, B, sfA, sfB, m_indices
+    g, init = run_contiguous(A, B, sfA, sfB, m_indices)
+    check_contiguous_full(w, g, init, exact=True)
+
+
 def test_masked_many_experts_bitwise():
     # more than 64 experts: the device-side tile schedule scans the counts in
     # several 64-wide chunks; empty experts sit at chunk edges
