@@ -94,7 +94,7 @@ TailSplit pipe_tail_split(int64_t tiles, int64_t KB) {
   return t;
 }
 
-template <class Cfg, int KIND>
+template <class Cfg, int KIND, int LAY = 0>
 dg_status launch_pipe(const Problem& p0, int64_t blocks, hipStream_t stream) {
   PipeArgs a{};
   a.p = p0;
@@ -120,7 +120,8 @@ dg_status launch_pipe(const Problem& p0, int64_t blocks, hipStream_t stream) {
   }
   a.items = (int32_t)grid;
   const int64_t wgs = grid < kCUs ? grid : kCUs;  // persistent, one workgroup per CU
-  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND>), dim3((unsigned)wgs), dim3(Cfg::NT), 0, stream, a);
+  hipLaunchKernelGGL((pipe_kernel<Cfg, KIND, false, LAY>), dim3((unsigned)wgs), dim3(Cfg::NT), 0,
+                     stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
   return DG_OK;
@@ -839,8 +840,19 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_swiglu(const void* A, const void* B, v
 namespace dg {
 namespace {
 
-// C = op(A) op(B): operands not stored K-contiguous (A as [K][M], B as [K][N]) are
-// first transposed into the stream's workspace, then the NT kernels run on them.
+// C = op(A) op(B) with A stored [K][M] (a_t) and/or B stored [K][N] (b_n). Shapes the
+// compute-bound kernel serves read such operands in place: their tiles are staged as
+// k-rows and transposed on the way from LDS into the MFMA (kLayAT / kLayBN). The
+// other kernels (M <= 64, or K past the compute-bound kernel's range) take
+// K-contiguous operands only: there the operand is first transposed into the stream's
+// workspace and the NT kernels run on the copy.
+template <int LAY>
+dg_status launch_layout(int id, const Problem& p, hipStream_t st) {
+  if (strcmp(kTable[id].name, "pipe256x128") == 0)
+    return launch_pipe<Pipe256x128, kDense, LAY>(p, 1, st);
+  return launch_pipe<Pipe128x256, kDense, LAY>(p, 1, st);
+}
+
 dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
                       const float* sfB, int64_t M, int64_t N, int64_t K, bool a_t, bool b_n,
                       void* stream) {
@@ -850,6 +862,28 @@ dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
   if (s != DG_OK || M == 0 || N == 0) return s;
   if (M > (int64_t)1 << 30) return fail(DG_ERR_UNSUPPORTED_SHAPE, "M beyond 2^30");
   const hipStream_t st = (hipStream_t)stream;
+  const int id = select_config(kDense, M, M, N, K, 1);
+  const bool pipe = strncmp(kTable[id].name, "pipe", 4) == 0;
+  // in place: 32-bit buffer offsets reach every byte of an MN-contiguous operand, and
+  // its k-rows start 16-byte aligned (N % 16 == 0 always; M % 16 for A stored [K][M])
+  const int64_t lim = (int64_t)1 << 31;
+  if (pipe && (!a_t || (K * M < lim && M % 16 == 0)) && (!b_n || K * N < lim)) {
+    maybe_print(kDense, M, N, K, 1, id);
+    Problem p{};
+    p.A = (const uint8_t*)A;
+    p.B = (const uint8_t*)B;
+    p.C = (uint16_t*)C;
+    p.sfA = (const uint8_t*)sfA;
+    p.sfB = sfB;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.G = 1;
+    const int lay = (a_t ? kLayAT : 0) | (b_n ? kLayBN : 0);
+    return lay == kLayBN ? launch_layout<kLayBN>(id, p, st)
+         : lay == kLayAT ? launch_layout<kLayAT>(id, p, st)
+                         : launch_layout<kLayAT | kLayBN>(id, p, st);
+  }
   uint8_t *a2 = nullptr, *b2 = nullptr;
   s = get_transpose_workspace(st, a_t ? (size_t)(M * K) : 0, b_n ? (size_t)(N * K) : 0, &a2, &b2);
   if (s != DG_OK) return s;

@@ -113,13 +113,22 @@ __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, in
   tn = idx / gsize;
 }
 
+// Operand memory layouts of the dense GEMM (bit set: the operand is stored with M or
+// N contiguous, i.e. as [K][M] or [K][N], instead of K-contiguous rows): the other
+// layouts of one GEMM family, C = op(A) op(B) with A stored [K][M] (T) and B stored
+// [K][N] (N) (DeepGEMM project page, aiproducthub.cn, "core features").
+constexpr int kLayAT = 1, kLayBN = 2;
+
 // DMA sources of one thread: buffer resources for the tile's rows (wave-uniform,
 // SGPRs) plus 32-bit per-lane byte offsets; the K-block offset goes in the
-// instruction's scalar offset. The scale resources end exactly at the end of sfA
-// and sfB, so reads past the last K-block of the last row return zero.
+// instruction's scalar offset (a_kstep / b_kstep bytes per K-block: 128 for a
+// K-contiguous operand, 128 rows of the stored matrix for an MN-contiguous one). The
+// scale resources end exactly at the end of sfA and sfB, so reads past the last
+// K-block of the last row return zero.
 template <class Cfg>
 struct PipeThread {
   __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc, sa_rsrc, sb_rsrc;
+  uint32_t a_kstep, b_kstep;
   uint32_t a_off[Cfg::A_DMA];
   uint32_t b_off[Cfg::B_DMA];
   uint32_t sa_off;  // this lane's sfA row
@@ -151,16 +160,16 @@ __device__ __forceinline__ void pipe_issue(const PipeThread<Cfg>& th, int kb, in
                                              0, 0);
   }
   uint8_t* st = pipe_stage<S>();
-  const int koff = kb * kKBlock;
+  const int koff_a = kb * th.a_kstep, koff_b = kb * th.b_kstep;
 #pragma unroll
   for (int q = 0; q < Cfg::A_DMA; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(th.a_rsrc, DG_LDS(st + (wave * Cfg::A_DMA + q) * 1024),
-                                             16, th.a_off[q], koff, 0, 0);
+                                             16, th.a_off[q], koff_a, 0, 0);
 #pragma unroll
   for (int q = 0; q < Cfg::B_DMA; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        th.b_rsrc, DG_LDS(st + Cfg::OFF_B + (wave * Cfg::B_DMA + q) * 1024), 16, th.b_off[q], koff,
-        0, 0);
+        th.b_rsrc, DG_LDS(st + Cfg::OFF_B + (wave * Cfg::B_DMA + q) * 1024), 16, th.b_off[q],
+        koff_b, 0, 0);
 #endif
 }
 
@@ -178,17 +187,17 @@ __device__ __forceinline__ void pipe_issue_ops(const PipeThread<Cfg>& th, int kb
                                              0, 0);
   }
   uint8_t* st = pipe_stage<S>();
-  const int koff = kb * kKBlock;
+  const int koff_a = kb * th.a_kstep, koff_b = kb * th.b_kstep;
 #pragma unroll
   for (int q = LO; q < HI; ++q) {
     if (q < Cfg::A_DMA)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(th.a_rsrc,
                                                DG_LDS(st + (wave * Cfg::A_DMA + q) * 1024), 16,
-                                               th.a_off[q], koff, 0, 0);
+                                               th.a_off[q], koff_a, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           th.b_rsrc, DG_LDS(st + Cfg::OFF_B + (wave * Cfg::B_DMA + q - Cfg::A_DMA) * 1024), 16,
-          th.b_off[q - Cfg::A_DMA], koff, 0, 0);
+          th.b_off[q - Cfg::A_DMA], koff_b, 0, 0);
   }
 #endif
 }
@@ -229,11 +238,38 @@ __device__ __forceinline__ void promote8(v16f& acc, const v16f& p, float s) {
 // 1), g = lane / 32. The swizzle depends on the row only through lane % 32 (tile
 // and wave offsets are multiples of 32 rows), so four byte offsets per operand
 // serve every tile; tile 1 is 4096 bytes further.
-template <class Cfg>
+//
+// An MN-contiguous operand (layout bit set) is staged as 128 k-rows of ROW = BM or BN
+// bytes (its tile's rows m or n along each k-row), and its 16-byte chunk c of k-row
+// k sits at chunk c ^ tswz(k) (tswz below). A fragment is then assembled from four
+// transposing 8-byte reads (ds_read_b64_tr_b8), each giving 8 consecutive k of one
+// row: in a group of 16 lanes, lanes 2j and 2j+1 point at the two 8-byte halves of
+// the 16 consecutive rows of k-row k0 + j, and lane i receives row i of those 16 at
+// k0..k0+7. For MFMA lane (r32, g) of tile t, group q = lane / 16 covers rows
+// 32t + 16 (q % 2) + 0..15 and k = 32 (q / 2) + 8d + 0..7 in read d. Only two per-lane
+// offsets per operand are kept (tile 0 and tile 1); the k-row of read d and K half h
+// is the immediate (64h + 8d) * ROW.
+__device__ __forceinline__ int tswz(int k, int row_chunks) {
+  // 8 consecutive k-rows x the 2 chunks of one 32-row tile hit 16 distinct chunk
+  // positions of a 64-bank LDS: whole rows of 16 chunks spread k mod 8 over chunk
+  // bits 1..3; half rows (8 chunks, two k-rows per bank sweep) spread k mod 8 / 2
+  return row_chunks == 16 ? 2 * (k & 7) : 2 * ((k & 7) >> 1);
+}
+
+template <class Cfg, int LAY>
 struct PipeLane {
-  uint32_t va[4], vb[4];
+  uint32_t va[4], vb[4];  // MN-contiguous operand: [0], [1] = tile 0, tile 1
   uint32_t sa0, sa1;  // byte offsets in pipe_scale of this lane's two A rows
   uint32_t sb;        // byte offset in pipe_sfb of the wave's sfB row
+  // per-lane offset of the transposing reads of 32-row tile t of an MN-contiguous
+  // operand whose wave slice starts at row r0 of a tile ROW bytes wide
+  template <int ROW>
+  __device__ __forceinline__ static uint32_t toff(int lane, int r0, int t) {
+    const int q = lane >> 4, p = lane & 15, j = p >> 1, half = p & 1;
+    const int krow = 32 * (q >> 1) + j;
+    const int c = (r0 + 32 * t + 16 * (q & 1)) >> 4;
+    return (uint32_t)(krow * ROW + ((c ^ tswz(krow, ROW / 16)) << 4) + 8 * half);
+  }
   __device__ __forceinline__ PipeLane(int wave, int lane) {
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
     const int r32 = lane & 31, g = lane >> 5;
@@ -244,6 +280,14 @@ struct PipeLane {
       const uint32_t c = (uint32_t)((chunk[k] ^ sw) << 4);
       va[k] = (uint32_t)(wm * 64 + r32) * kKBlock + c;
       vb[k] = (uint32_t)Cfg::OFF_B + (uint32_t)(wn * 64 + r32) * kKBlock + c;
+    }
+    if (LAY & kLayAT) {
+      va[0] = toff<Cfg::BM>(lane, wm * 64, 0);
+      va[1] = toff<Cfg::BM>(lane, wm * 64, 1);
+    }
+    if (LAY & kLayBN) {
+      vb[0] = (uint32_t)Cfg::OFF_B + toff<Cfg::BN>(lane, wn * 64, 0);
+      vb[1] = (uint32_t)Cfg::OFF_B + toff<Cfg::BN>(lane, wn * 64, 1);
     }
     const int ra0 = wm * 64 + r32, ra1 = ra0 + 32;
     sa0 = (uint32_t)((ra0 / Cfg::RPW) * kScaleWaveBytes + (ra0 % Cfg::RPW) * 16);
@@ -259,6 +303,45 @@ __device__ __forceinline__ void read_tile(const uint8_t* st, const uint32_t (&v)
   const uint8_t* p = st + tile * 32 * kKBlock;
   h0 = frag_at(p, v[0], v[1]);
   h1 = frag_at(p, v[2], v[3]);
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v2i tr8_at(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
+}
+
+// The same fragments of an MN-contiguous operand staged as k-rows of ROW bytes: four
+// transposing reads per K half (see PipeLane).
+template <int ROW>
+__device__ __forceinline__ void read_tile_t(const uint8_t* st, const uint32_t (&v)[4], int tile,
+                                            v8i& h0, v8i& h1) {
+  const uint8_t* p = st + v[tile];
+  const v2i a0 = tr8_at(p), a1 = tr8_at(p + 8 * ROW), a2 = tr8_at(p + 16 * ROW),
+            a3 = tr8_at(p + 24 * ROW);
+  const v2i b0 = tr8_at(p + 64 * ROW), b1 = tr8_at(p + 72 * ROW), b2 = tr8_at(p + 80 * ROW),
+            b3 = tr8_at(p + 88 * ROW);
+  h0 = v8i{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+  h1 = v8i{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+}
+
+// A-tile and B-tile fragment reads in the operand's layout.
+template <class Cfg, int LAY>
+__device__ __forceinline__ void read_a(const uint8_t* st, const PipeLane<Cfg, LAY>& pl, int tile,
+                                       v8i& h0, v8i& h1) {
+  if (LAY & kLayAT)
+    read_tile_t<Cfg::BM>(st, pl.va, tile, h0, h1);
+  else
+    read_tile(st, pl.va, tile, h0, h1);
+}
+
+template <class Cfg, int LAY>
+__device__ __forceinline__ void read_b(const uint8_t* st, const PipeLane<Cfg, LAY>& pl, int tile,
+                                       v8i& h0, v8i& h1) {
+  if (LAY & kLayBN)
+    read_tile_t<Cfg::BN>(st, pl.vb, tile, h0, h1);
+  else
+    read_tile(st, pl.vb, tile, h0, h1);
 }
 
 // Fragments a K-block's step starts with: A tile 0 and both B tiles, read during
@@ -284,8 +367,8 @@ struct PipeScales {
 // B tile 1 of kb+1 are read (B tile 1 into spare registers). B tile 0 of kb+1 is
 // read after M7, when kb's is dead. Scheduling fences keep this order; the compiler
 // inserts only the LDS waits.
-template <class Cfg, int S, int MODE>
-__device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeLane<Cfg>& pl,
+template <class Cfg, int S, int MODE, int LAY>
+__device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeLane<Cfg, LAY>& pl,
                                           v16f (&acc)[2][2], Frag0& f, v16f (&carry)[2],
                                           float& carry_s, PipeScales& sc, int kb, int KB,
                                           int wave) {
@@ -304,7 +387,7 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   const v16f zero = {};
 
   v8i a10, a11;
-  if (HI) read_tile(st, pl.va, 1, a10, a11);
+  if (HI) read_a(st, pl, 1, a10, a11);
   if (S == 0) {
     // scales of K-blocks kb..kb+2 (landed before the previous barrier): three fp32
     // values, or (packed) bytes kb % 4 .. kb % 4 + 2 of the words from kb / 4 on
@@ -356,13 +439,13 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   __builtin_amdgcn_s_barrier();
   DG_FENCE();
   const float s0 = sc.s0[S], s1 = sc.s1[S];
-  read_tile(nst, pl.va, 0, f.a0, f.a1);
+  read_a(nst, pl, 0, f.a0, f.a1);
   DG_FENCE();
   v16f p10, p11;
   if (HI) p10 = mfma32(f.b0, a10, zero);  // M5
   pipe_issue_ops<Cfg, S, S == 0, 0, Q1>(th, kn, wave);
   v8i c0n, c1n;
-  read_tile(nst, pl.vb, 1, c0n, c1n);
+  read_b(nst, pl, 1, c0n, c1n);
   promote8<0>(acc[0][0], p00, s0);
   DG_FENCE();
   if (HI) p11 = mfma32(f.c0, a10, zero);  // M6
@@ -373,7 +456,7 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   pipe_issue_ops<Cfg, S, false, Q2, Q3>(th, kn, wave);
   promote8<0>(acc[0][1], p01, s0);
   DG_FENCE();
-  read_tile(nst, pl.vb, 0, f.b0, f.b1);
+  read_b(nst, pl, 0, f.b0, f.b1);
   DG_FENCE();
   if (HI) p11 = mfma32(f.c1, a11, p11);  // M8
   pipe_issue_ops<Cfg, S, false, Q3, OPS>(th, kn, wave);
@@ -398,7 +481,7 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
 // stays zero); MODE 2: the whole sub-tile.
 // b_hi: tile rows from 128 on come from B rows b_hi further on (and their sfB blocks
 // likewise): the up half of a [gate; up] B, b_hi = I - 128. 0 for a plain tile.
-template <class Cfg, int MODE>
+template <class Cfg, int MODE, int LAY>
 __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileView& v, int kb_lo,
                                                  int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN],
                                                  int b_hi) {
@@ -417,9 +500,23 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
     const int a_rows = (int)(v.rows - v.m0 < Cfg::BM ? v.rows - v.m0 : Cfg::BM);
     const int b_rows = (int)(N - v.n0 < Cfg::BN ? N - v.n0 : Cfg::BN);
     // rows past the ends are out of the resources' range: the DMA writes zeros and
-    // fetches nothing
-    th.a_rsrc = raw_rsrc(v.A + v.m0 * K, (int64_t)a_rows * K);
-    th.b_rsrc = raw_rsrc(v.B + v.n0 * K, (int64_t)(b_hi ? Cfg::BN + b_hi : b_rows) * K);
+    // fetches nothing. An MN-contiguous operand's tile is a column range of every
+    // stored k-row; its resource runs to the end of the matrix, and chunks past M or N
+    // are redirected to the last valid chunk of the k-row (below).
+    if (LAY & kLayAT) {
+      th.a_rsrc = raw_rsrc(v.A + v.m0, K * v.rows - v.m0);
+      th.a_kstep = (uint32_t)(kKBlock * v.rows);
+    } else {
+      th.a_rsrc = raw_rsrc(v.A + v.m0 * K, (int64_t)a_rows * K);
+      th.a_kstep = kKBlock;
+    }
+    if (LAY & kLayBN) {
+      th.b_rsrc = raw_rsrc(v.B + v.n0, K * N - v.n0);
+      th.b_kstep = (uint32_t)(kKBlock * N);
+    } else {
+      th.b_rsrc = raw_rsrc(v.B + v.n0 * K, (int64_t)(b_hi ? Cfg::BN + b_hi : b_rows) * K);
+      th.b_kstep = kKBlock;
+    }
     const int64_t rb = sfa_row_bytes(KB, p.sfa_packed);
     th.sa_rsrc = raw_rsrc(v.sfA + v.m0 * rb, (v.rows - v.m0) * rb);
     th.sa_shift = p.sfa_packed ? 2 : 0;
@@ -427,14 +524,36 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
     const int rsub = lane >> 3, c = lane & 7;
 #pragma unroll
     for (int q = 0; q < Cfg::A_DMA; ++q) {
-      const int R = (wave * Cfg::A_DMA + q) * 8 + rsub;
-      th.a_off[q] = (uint32_t)R * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+      if (LAY & kLayAT) {
+        // the DMA's 1 KB fills k-rows of BM bytes in order; lane l writes LDS chunk pc
+        // of its k-row, which holds stored chunk pc ^ tswz(k)
+        const int byte = (wave * Cfg::A_DMA + q) * 1024 + 16 * lane;
+        const int kr = byte / Cfg::BM, pc = (byte % Cfg::BM) >> 4;
+        // a chunk past the last row m re-reads the last valid chunk of its k-row, so
+        // every address stays inside A (those rows are never stored)
+        const int valid = (int)((v.rows - v.m0) >> 4);
+        int lc = pc ^ tswz(kr, Cfg::BM / 16);
+        if (lc >= valid) lc = valid - 1;
+        th.a_off[q] = (uint32_t)kr * (uint32_t)v.rows + (uint32_t)(lc << 4);
+      } else {
+        const int R = (wave * Cfg::A_DMA + q) * 8 + rsub;
+        th.a_off[q] = (uint32_t)R * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+      }
     }
 #pragma unroll
     for (int q = 0; q < Cfg::B_DMA; ++q) {
-      const int R = (wave * Cfg::B_DMA + q) * 8 + rsub;
-      const int Rg = R + (R >= 128 ? b_hi : 0);  // row of B (relative to n0)
-      th.b_off[q] = (uint32_t)Rg * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+      if (LAY & kLayBN) {
+        const int byte = (wave * Cfg::B_DMA + q) * 1024 + 16 * lane;
+        const int kr = byte / Cfg::BN, pc = (byte % Cfg::BN) >> 4;
+        const int valid = (int)((N - v.n0) >> 4);  // N % 16 == 0
+        int lc = pc ^ tswz(kr, Cfg::BN / 16);
+        if (lc >= valid) lc = valid - 1;
+        th.b_off[q] = (uint32_t)kr * (uint32_t)N + (uint32_t)(lc << 4);
+      } else {
+        const int R = (wave * Cfg::B_DMA + q) * 8 + rsub;
+        const int Rg = R + (R >= 128 ? b_hi : 0);  // row of B (relative to n0)
+        th.b_off[q] = (uint32_t)Rg * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+      }
     }
     int arow = wave * Cfg::RPW + (lane % Cfg::RPW);
     if (arow >= a_rows) arow = a_rows - 1;
@@ -451,7 +570,7 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
     for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
   v16f carry[2] = {v16f{}, v16f{}};
   float carry_s = 0.f;
-  const PipeLane<Cfg> pl(wave, lane);
+  const PipeLane<Cfg, LAY> pl(wave, lane);
   Frag0 f;
   PipeScales sc;
 
@@ -466,20 +585,20 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
   pipe_issue<Cfg, 2, false>(th, kb_lo + 2 < kb_hi ? kb_lo + 2 : kb_hi - 1, wave);
   DG_FENCE();
   if (MODE > 0) {
-    read_tile(read_base<0>(), pl.va, 0, f.a0, f.a1);
-    read_tile(read_base<0>(), pl.vb, 0, f.b0, f.b1);
-    read_tile(read_base<0>(), pl.vb, 1, f.c0, f.c1);
+    read_a(read_base<0>(), pl, 0, f.a0, f.a1);
+    read_b(read_base<0>(), pl, 0, f.b0, f.b1);
+    read_b(read_base<0>(), pl, 1, f.c0, f.c1);
   }
   DG_FENCE();
   int kb = kb_lo;
   for (; kb + 3 <= kb_hi; kb += 3) {
-    pipe_step<Cfg, 0, MODE>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
-    pipe_step<Cfg, 1, MODE>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
-    pipe_step<Cfg, 2, MODE>(th, pl, acc, f, carry, carry_s, sc, kb + 2, kb_hi, wave);
+    pipe_step<Cfg, 0, MODE, LAY>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
+    pipe_step<Cfg, 1, MODE, LAY>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
+    pipe_step<Cfg, 2, MODE, LAY>(th, pl, acc, f, carry, carry_s, sc, kb + 2, kb_hi, wave);
   }
-  if (kb < kb_hi) pipe_step<Cfg, 0, MODE>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
+  if (kb < kb_hi) pipe_step<Cfg, 0, MODE, LAY>(th, pl, acc, f, carry, carry_s, sc, kb, kb_hi, wave);
   if (kb + 1 < kb_hi)
-    pipe_step<Cfg, 1, MODE>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
+    pipe_step<Cfg, 1, MODE, LAY>(th, pl, acc, f, carry, carry_s, sc, kb + 1, kb_hi, wave);
   if (MODE == 2) {
     promote8<0>(acc[1][0], carry[0], carry_s);
     promote8<8>(acc[1][0], carry[0], carry_s);
@@ -497,7 +616,7 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
 // row is below v.rows and the sub-tile's first column below N; `quarters` (bit q for
 // the tile's 32-row quarter q) lets the caller rule out quarters whose rows are all
 // someone else's (contiguous layout). The three modes pass the same barriers.
-template <class Cfg>
+template <class Cfg, int LAY = 0>
 __device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& v, int kb_lo,
                                               int kb_hi, v16f (&acc)[Cfg::TM][Cfg::TN],
                                               uint32_t quarters = ~0u, int b_hi = 0) {
@@ -507,11 +626,11 @@ __device__ __forceinline__ void pipe_mainloop(const Problem& p, const TileView& 
   const bool lo = cols && ((quarters >> (2 * wm)) & 1) && v.m0 + wm * 64 < v.rows;
   const bool hi = cols && ((quarters >> (2 * wm + 1)) & 1) && v.m0 + wm * 64 + 32 < v.rows;
   if (hi)
-    pipe_mainloop_as<Cfg, 2>(p, v, kb_lo, kb_hi, acc, b_hi);
+    pipe_mainloop_as<Cfg, 2, LAY>(p, v, kb_lo, kb_hi, acc, b_hi);
   else if (lo)
-    pipe_mainloop_as<Cfg, 1>(p, v, kb_lo, kb_hi, acc, b_hi);
+    pipe_mainloop_as<Cfg, 1, LAY>(p, v, kb_lo, kb_hi, acc, b_hi);
   else
-    pipe_mainloop_as<Cfg, 0>(p, v, kb_lo, kb_hi, acc, b_hi);
+    pipe_mainloop_as<Cfg, 0, LAY>(p, v, kb_lo, kb_hi, acc, b_hi);
 }
 
 // bf16 RNE store of a finished tile: produced rows (< valid_rows, and for the
@@ -670,7 +789,7 @@ __device__ __forceinline__ void pipe_store_swiglu(const Problem& p, const TileVi
   __syncthreads();  // the LDS is free again (the contiguous layout may run another pass)
 }
 
-template <class Cfg, int KIND, bool SWIGLU = false>
+template <class Cfg, int KIND, bool SWIGLU = false, int LAY = 0>
 __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, int expert,
                                           int valid_rows, uint32_t quarters = ~0u,
                                           SwigluOut sw = SwigluOut{}) {
@@ -679,7 +798,7 @@ __device__ __forceinline__ void pipe_tile(const Problem& p, const TileView& v, i
     pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, quarters, sw.I - 128);
     pipe_store_swiglu<Cfg, KIND>(p, v, expert, valid_rows, acc, sw);
   } else {
-    pipe_mainloop<Cfg>(p, v, 0, (int)(p.K / kKBlock), acc, quarters);
+    pipe_mainloop<Cfg, LAY>(p, v, 0, (int)(p.K / kKBlock), acc, quarters);
     pipe_store<Cfg, KIND>(p, v, expert, valid_rows, acc);
   }
 }
@@ -754,12 +873,12 @@ struct PipeArgs {
 // tiles), part `part` of `parts`. Each part writes its fp32 tile with device-scope
 // stores and counts its arrival; the last part to arrive adds the parts in part
 // order -- a fixed order, so the result is deterministic -- and stores bf16.
-template <class Cfg>
+template <class Cfg, int LAY>
 __device__ __forceinline__ void pipe_split_tile(const PipeArgs& a, const TileView& v, int tt,
                                                 int part, int kb_lo, int kb_hi) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN, BMN = Cfg::BM * Cfg::BN;
   v16f acc[TM][TN];
-  pipe_mainloop<Cfg>(a.p, v, kb_lo, kb_hi, acc);
+  pipe_mainloop<Cfg, LAY>(a.p, v, kb_lo, kb_hi, acc);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
       a.ws + (int64_t)tt * a.parts * BMN, 0, 0x7FFFFFFF, 0x00020000);
@@ -822,8 +941,9 @@ __device__ __forceinline__ void pipe_split_tile(const PipeArgs& a, const TileVie
 // SWIGLU (grouped layouts, 128x256 tiles): B is [gate; up] with 2 * sw.I rows per
 // expert, tile tn covers gate columns 128 tn.. and the matching up columns, and the
 // fused epilogue writes quantized h instead of bf16 C.
-template <class Cfg, int KIND, bool SWIGLU>
+template <class Cfg, int KIND, bool SWIGLU, int LAY>
 __device__ __forceinline__ void pipe_item(const PipeArgs& args, int item) {
+  static_assert(LAY == 0 || (KIND == kDense && !SWIGLU), "other layouts: dense GEMM only");
   static_assert(!SWIGLU || KIND != kDense, "the fused epilogue is for the grouped layouts");
   constexpr int NSTEP = SWIGLU ? 128 : Cfg::BN;  // columns between consecutive N-tiles
   const Problem& p = args.p;
@@ -842,7 +962,8 @@ __device__ __forceinline__ void pipe_item(const PipeArgs& args, int item) {
     v.rows = p.M;
     v.B = p.B;
     v.sfB = p.sfB;
-    pipe_split_tile<Cfg>(args, v, tt, part, part * KB / args.parts, (part + 1) * KB / args.parts);
+    pipe_split_tile<Cfg, LAY>(args, v, tt, part, part * KB / args.parts,
+                              (part + 1) * KB / args.parts);
     return;
   }
   const int NB = (int)((p.N + kKBlock - 1) / kKBlock);
@@ -881,7 +1002,7 @@ __device__ __forceinline__ void pipe_item(const PipeArgs& args, int item) {
   if (KIND == kDense) {
     v.B = p.B;
     v.sfB = p.sfB;
-    pipe_tile<Cfg, KIND>(p, v, 0, (int)p.M);
+    pipe_tile<Cfg, KIND, false, LAY>(p, v, 0, (int)p.M);
     return;
   }
   // contiguous: one pass per distinct expert id among the tile's rows, in
@@ -921,10 +1042,10 @@ __device__ __forceinline__ void pipe_item(const PipeArgs& args, int item) {
 // blockIdx.x + gridDim.x, ... (gridDim.x is the item count, or a multiple of 8 when
 // smaller, so item i stays on XCD i % 8). A tile's stores drain while the next
 // tile's first DMAs are in flight, and no workgroup is dispatched per tile.
-template <class Cfg, int KIND, bool SWIGLU = false>
+template <class Cfg, int KIND, bool SWIGLU = false, int LAY = 0>
 __global__ void __launch_bounds__(Cfg::NT) pipe_kernel(PipeArgs args) {
   for (int item = blockIdx.x; item < args.items; item += gridDim.x)
-    pipe_item<Cfg, KIND, SWIGLU>(args, item);
+    pipe_item<Cfg, KIND, SWIGLU, LAY>(args, item);
 }
 
 }  // namespace dg

@@ -2,8 +2,14 @@
 oracle's layout GEMM (strided indexing of the stored operands) must match bit for bit
 on integer-valued inputs and within the tolerance on N(0,1) inputs; and each call
 must equal dg_fp8_gemm_nt on transposed copies of its operands bit for bit, up to the
-full prefill shape. Shapes cover odd M (the transposition's unaligned path), N tails,
-M = 1, and M <= 64 (decode kernels) as well as the compute-bound kernel."""
+full prefill shape.
+
+Two paths serve these calls. Shapes of the compute-bound kernel (M > 64) read the
+[K][M] / [K][N] operands in place (k-row tiles, transposing LDS reads): covered on
+both tile shapes, M and N tails, the dense tail split, long K, and by capture into a
+HIP graph on a fresh stream, which succeeds only because nothing is allocated. M <= 64
+and A stored [K][M] with M % 16 != 0 go through a transposed copy: odd M, M = 1 and the
+decode kernels cover that path."""
 import numpy as np
 import pytest
 import torch
@@ -66,3 +72,57 @@ def test_prefill_shape_equals_nt(layout):
     A, B = stored(w.A, w.B, layout)
     assert np.array_equal(run(layout, A, B, w.sfA, w.sfB, M, N),
                           run("nt", w.A, w.B, w.sfA, w.sfB, M, N))
+
+
+NATIVE = [(128, 256, 512), (144, 272, 384), (256, 1040, 1152), (384, 768, 2048),
+          (208, 4096, 256), (320, 400, 8192)]
+
+
+@pytest.mark.parametrize("cfg", ["pipe256x128", "pipe128x256"])
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_native_layouts_every_tile_shape_bitwise(cfg, layout, monkeypatch):
+    """In-place reads of MN-contiguous operands on both tile shapes: N tails of 16
+    columns, M tails, the dense tail split (384x768x2048) and a long K."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    for (M, N, K) in NATIVE:
+        rng = np.random.default_rng(M + 3 * N + 7 * K + ord(layout[0]) + 5 * ord(layout[1]))
+        A_mk, B_nk, sfA, sfB = int_operands(rng, M, N, K)
+        A, B = stored(A_mk, B_nk, layout)
+        g = run(layout, A, B, sfA, sfB, M, N)
+        assert_bitwise(g, oracle.gemm(A, B, sfA, sfB, layout), what=f"{cfg} {layout} {M}x{N}x{K}")
+        assert np.array_equal(g, run("nt", A_mk, B_nk, sfA, sfB, M, N))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_native_layout_gaussian(layout):
+    M, N, K = 208, 528, 1536
+    w = synth.dense(M, N, K, 779000)
+    A, B = stored(w.A, w.B, layout)
+    g = run(layout, A, B, w.sfA, w.sfB, M, N)
+    print(layout, assert_parity(g, oracle.gemm(A, B, w.sfA, w.sfB, layout), what=layout))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_native_layout_allocates_nothing(layout):
+    """256x1024x512 (whole rounds of tiles, no split): captured into a HIP graph on a
+    stream where nothing ran before. The copy path would need a workspace and fail
+    with DG_ERR_CAPTURE; the in-place path records only its kernel."""
+    import fp8_block_scaled_dg_amd as dg
+    M, N, K = 256, 1024, 512
+    rng = np.random.default_rng(11 + ord(layout[0]) + ord(layout[1]))
+    A_mk, B_nk, sfA, sfB = int_operands(rng, M, N, K)
+    A, B = stored(A_mk, B_nk, layout)
+    a, b, sa, sb = gu.codes(A), gu.codes(B), gu.dev(sfA), gu.dev(sfB)
+    c = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    gu.announce(f"native {layout} under capture")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        getattr(dg, "fp8_gemm_" + layout)(a, b, c, sa, sb)
+    for rep in range(3):
+        c.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = c.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert_bitwise(got, oracle.gemm(A, B, sfA, sfB, layout), what=f"{layout} replay {rep}")
