@@ -862,7 +862,12 @@ dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
   if (s != DG_OK || M == 0 || N == 0) return s;
   if (M > (int64_t)1 << 30) return fail(DG_ERR_UNSUPPORTED_SHAPE, "M beyond 2^30");
   const hipStream_t st = (hipStream_t)stream;
-  const int id = select_config(kDense, M, M, N, K, 1);
+  int id = select_config(kDense, M, M, N, K, 1);
+  // M <= 64 with B stored [K][N] and at most 8 K-blocks: the 128x256-tile kernel in
+  // place beats transposing B for the M <= 64 kernels (64x32768x512 NN: 11.5 against
+  // 16.5 us); with long K the copy wins (64x2112x7168 NN: 21.1 against 24.6 us)
+  const char* forced = getenv("DG_FORCE_CONFIG");
+  if (M <= 64 && b_n && K / kKBlock <= 8 && !(forced && *forced)) id = find_cfg("pipe128x256");
   const bool pipe = strncmp(kTable[id].name, "pipe", 4) == 0;
   // in place: 32-bit buffer offsets reach every byte of an MN-contiguous operand, and
   // its k-rows start 16-byte aligned (N % 16 == 0 always; M % 16 for A stored [K][M])
