@@ -142,6 +142,31 @@ def test_dense_deterministic():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("kind", ["dec32768", "tail_split", "contiguous", "masked"])
+def test_deterministic_across_calls(kind):
+    """Same inputs, same bits: split-K with its last-arriver reduction (64x32768x512
+    and the dense tail split), and both grouped layouts with their device-side tile
+    schedules, each called twice into differently filled outputs."""
+    if kind in ("dec32768", "tail_split"):
+        w = synth.workload("dec32768") if kind == "dec32768" else synth.dense(384, 768, 2048, 881000)
+        a = run_dense(w.A, w.B, w.sfA, w.sfB, seed=5)
+        b = run_dense(w.A, w.B, w.sfA, w.sfB, seed=6)
+        assert np.array_equal(a, b)
+    elif kind == "contiguous":
+        counts = np.array([300, 0, 17, 129, 256, 1], dtype=np.int32)
+        w = synth.contiguous(6, 512, 1024, 0, seed_base=882000, counts=counts)
+        (a, _), (b, _) = (run_contiguous(w.A, w.B, w.sfA, w.sfB, w.m_indices, seed=s)
+                          for s in (5, 6))
+        pad = w.m_indices < 0
+        assert np.array_equal(a[~pad], b[~pad])
+    else:
+        masked_m = np.array([200, 0, 77, 256, 31], dtype=np.int32)
+        w = synth.masked(5, 256, 768, 1024, seed_base=883000, masked_m=masked_m)
+        (a, _), (b, _) = (run_masked(w.A, w.B, w.sfA, w.sfB, w.masked_m, seed=s) for s in (5, 6))
+        produced = np.arange(256)[None, :] < masked_m[:, None]
+        assert np.array_equal(a[produced], b[produced])
+
+
 @pytest.mark.parametrize("name", ["dec2112", "dec32768"])
 def test_decode_workloads_full(name):
     w = synth.workload(name)
