@@ -139,3 +139,49 @@ def test_error_model_gaussian(M, N, K, seed):
     rep = error_model_report(g, r, abs_product_sum(w.A, w.B, w.sfA, w.sfB))
     print(f"\n[model] {M}x{N}x{K}: {rep}", flush=True)
     assert rep["max_ratio"] <= parity.MFMA_EPS
+
+
+def adversarial_operands(rng, M, N, K):
+    """Groups built to be cut: per 8 consecutive K positions of each row of B one large
+    code and seven small ones spread around 2^-13 of it (subnormals and small
+    normals), against N(0,1)-like A codes."""
+    A = rng.choice(np.array([0x30, 0x34, 0x38, 0x3C, 0x40, 0xB8, 0xC0, 0x44, 0xC4], np.uint8),
+                   size=(M, K))
+    small = np.array([0x01, 0x02, 0x03, 0x05, 0x07, 0x08, 0x0B, 0x10, 0x13, 0x18, 0x1D,
+                      0x81, 0x86, 0x90, 0x98], np.uint8)
+    B = rng.choice(small, size=(N, K))
+    big = rng.integers(0, 8, size=(N, K // 8))
+    for j in range(K // 8):
+        B[np.arange(N), 8 * j + big[:, j]] = rng.choice(np.array([0x7E, 0x76, 0xFE, 0x6E], np.uint8), N)
+    sfA = np.ldexp(1.0, rng.integers(-3, 4, size=(M, K // 128))).astype(np.float32)
+    sfB = np.ldexp(1.0, rng.integers(-3, 4, size=((N + 127) // 128, K // 128))).astype(np.float32)
+    return A.astype(np.uint8), B.astype(np.uint8), sfA, sfB
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+@pytest.mark.parametrize("data", ["gaussian", "adversarial"])
+def test_per_output_model_bound(cfg, data, monkeypatch):
+    """Every output within ulp/2 of its fp32 value plus the model's per-output bound
+    (tests/parity.py model_bound); on the adversarial inputs the cut products make
+    the error far larger than on Gaussian data, and the bound still holds."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    M = _rows(cfg)
+    N, K = 272, 1024
+    rng = np.random.default_rng(len(cfg) * 31 + len(data))
+    if data == "gaussian":
+        w = synth.dense(M, N, K, seed_base=425000 + len(cfg))
+        A, B, sfA, sfB = w.A, w.B, w.sfA, w.sfB
+    else:
+        A, B, sfA, sfB = adversarial_operands(rng, M, N, K)
+    g = run_dense(A, B, sfA, sfB)
+    r = oracle.gemm_nt(A, B, sfA, sfB)
+    bound = parity.model_bound(A, B, sfA, sfB, k_roundings=K // 128 + 8)
+    gv = parity.bf16_to_f64(g)
+    hu = parity.half_ulp_bf16(np.abs(gv))
+    over = np.abs(gv - r) - hu
+    ratio = float(np.max(over / bound))
+    rabs = abs_product_sum(A, B, sfA, sfB)
+    flat = float(np.max(np.maximum(over, 0) / rabs))
+    print(f"\n[bound] {cfg} {data}: max (|g-r| - ulp/2) / bound = {ratio:.3g}; "
+          f"against R_abs {flat:.3g}", flush=True)
+    assert ratio <= 1.0
