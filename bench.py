@@ -656,6 +656,33 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def mfma_ceiling(iters: int = 2000, reps: int = 10):
+    """The matrix-instruction rate probe (libdg_probe.so): one workgroup of 8 waves per
+    CU, each wave 4 * iters FP8 32x32x64 MFMAs on random e4m3fn register operands,
+    graph-timed, with the gfx clock sampled meanwhile: (TFLOP/s, GHz or None)."""
+    import ctypes
+    import torch
+    from fp8_block_scaled_dg_amd import build as dgb
+    lib = ctypes.CDLL(dgb.PROBE_LIB_PATH)
+    lib.dg_probe_mfma_rate.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    blocks = 256
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda:0")
+
+    def launch(i):
+        rc = lib.dg_probe_mfma_rate(iters, blocks, 12345 + i, sink.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, rc
+    for i in range(3):
+        launch(i)
+    torch.cuda.synchronize()
+    sampler = ClockSampler()
+    ms = timed_launches(launch, reps, 0, True, sampler)
+    flops = blocks * 8 * 4 * iters * 2.0 * 32 * 32 * 64
+    mhz = sampler.mean()
+    return flops / (ms * 1e-3) / 1e12, (mhz / 1e3 if mhz else None)
+
+
 def prefill_leg(K: int, rotate: int, graph: bool) -> dict:
     """The compute-bound half of the metric: the dense prefill GEMM 4096x7168x18432,
     K launches timed like the step's GEMMs, against the dense FP8 MFMA peak; the shader
@@ -686,6 +713,9 @@ def prefill_leg(K: int, rotate: int, graph: bool) -> dict:
                 frac_at_clock=(tflops / (FP8_PEAK_TFLOPS * mhz / 1e3 / PEAK_CLOCK_GHZ))
                 if mhz else None,
                 clock_samples=len(sampler.samples))
+    ceil_tf, ceil_ghz = mfma_ceiling()
+    roof.update(ceiling_tflops=ceil_tf, ceiling_clock_ghz=ceil_ghz,
+                frac_of_ceiling=tflops / ceil_tf)
     # parity of the last timed launch on seeded whole rows
     import oracle
     from tests.parity import report
