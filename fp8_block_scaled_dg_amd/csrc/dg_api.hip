@@ -386,9 +386,10 @@ bool stream_fits(int64_t M, int64_t N, int64_t K) {
   return stream_plan<Cfg>(N, K).KS <= Cfg::D;
 }
 
-template <class Cfg>
+template <class Cfg, int LAY = 0>
 dg_status launch_stream(const Problem& p0, int64_t blocks, hipStream_t stream) {
   (void)blocks;
+  if (LAY != 0 && p0.sfa_packed) return fail(DG_ERR_UNSUPPORTED_SHAPE, "packed sfA with MN-contiguous operands");
   const StreamPlan pl = stream_plan<Cfg>(p0.N, p0.K);
   if (pl.KS > Cfg::D) return fail(DG_ERR_UNSUPPORTED_SHAPE, "K run %lld > %d", (long long)pl.KS, Cfg::D);
   StreamArgs a{};
@@ -402,7 +403,9 @@ dg_status launch_stream(const Problem& p0, int64_t blocks, hipStream_t stream) {
     dg_status st = get_workspace(stream, part, (size_t)pl.tiles, &a.ws, &a.counters);
     if (st != DG_OK) return st;
   }
-  if (p0.sfa_packed)
+  if (LAY != 0)
+    hipLaunchKernelGGL((stream_kernel<Cfg, false, LAY>), dim3((unsigned)pl.grid), dim3(Cfg::NT), 0, stream, a);
+  else if (p0.sfa_packed)
     hipLaunchKernelGGL((stream_kernel<Cfg, true>), dim3((unsigned)pl.grid), dim3(Cfg::NT), 0, stream, a);
   else
     hipLaunchKernelGGL((stream_kernel<Cfg, false>), dim3((unsigned)pl.grid), dim3(Cfg::NT), 0, stream, a);
@@ -841,16 +844,25 @@ namespace dg {
 namespace {
 
 // C = op(A) op(B) with A stored [K][M] (a_t) and/or B stored [K][N] (b_n). Shapes the
-// compute-bound kernel serves read such operands in place: their tiles are staged as
-// k-rows and transposed on the way from LDS into the MFMA (kLayAT / kLayBN). The
-// other kernels (M <= 64, or K past the compute-bound kernel's range) take
-// K-contiguous operands only: there the operand is first transposed into the stream's
-// workspace and the NT kernels run on the copy.
+// compute-bound kernel or the split-K decode kernel serves read such operands in
+// place: their tiles are staged as k-rows and transposed on the way from LDS into the
+// MFMA (kLayAT / kLayBN). The other kernels (the rolling M <= 64 kernel, the tiled
+// kernel past the compute-bound kernel's K range) take K-contiguous operands only:
+// there the operand is first transposed into the stream's workspace and the NT
+// kernels run on the copy.
 template <int LAY>
 dg_status launch_layout(int id, const Problem& p, hipStream_t st) {
-  if (strcmp(kTable[id].name, "pipe256x128") == 0)
-    return launch_pipe<Pipe256x128, kDense, LAY>(p, 1, st);
+  const char* name = kTable[id].name;
+  if (strcmp(name, "stream_w4_tn1_d10") == 0) return launch_stream<Stream1x10, LAY>(p, 1, st);
+  if (strcmp(name, "stream_w4_tn1_d4") == 0) return launch_stream<Stream1x4, LAY>(p, 1, st);
+  if (strcmp(name, "pipe256x128") == 0) return launch_pipe<Pipe256x128, kDense, LAY>(p, 1, st);
   return launch_pipe<Pipe128x256, kDense, LAY>(p, 1, st);
+}
+
+bool layout_in_place(int id) {
+  const char* name = kTable[id].name;
+  return strncmp(name, "pipe", 4) == 0 || strcmp(name, "stream_w4_tn1_d10") == 0 ||
+         strcmp(name, "stream_w4_tn1_d4") == 0;
 }
 
 dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
@@ -864,15 +876,20 @@ dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
   const hipStream_t st = (hipStream_t)stream;
   int id = select_config(kDense, M, M, N, K, 1);
   // M <= 64 with B stored [K][N] and at most 8 K-blocks: the 128x256-tile kernel in
-  // place beats transposing B for the M <= 64 kernels (64x32768x512 NN: 11.5 against
-  // 16.5 us); with long K the copy wins (64x2112x7168 NN: 21.1 against 24.6 us)
+  // place beats both transposing B for the rolling kernel and the split-K decode
+  // kernel in place (64x32768x512 NN: 11.5 against 16.5 and 15.0 us); with long K the
+  // decode kernel in place wins (64x2112x7168 NN: 13.1 against 21.1 us copied and
+  // 24.6 us on the 128x256-tile kernel)
   const char* forced = getenv("DG_FORCE_CONFIG");
   if (M <= 64 && b_n && K / kKBlock <= 8 && !(forced && *forced)) id = find_cfg("pipe128x256");
-  const bool pipe = strncmp(kTable[id].name, "pipe", 4) == 0;
-  // in place: 32-bit buffer offsets reach every byte of an MN-contiguous operand, and
-  // its k-rows start 16-byte aligned (N % 16 == 0 always; M % 16 for A stored [K][M])
-  const int64_t lim = (int64_t)1 << 31;
-  if (pipe && (!a_t || (K * M < lim && M % 16 == 0)) && (!b_n || K * N < lim)) {
+  const bool small_k = strncmp(kTable[id].name, "stream", 6) == 0;
+  // in place: 32-bit buffer offsets reach every byte of an MN-contiguous operand (the
+  // compute-bound kernel addresses all of K from one base, the M <= 64 kernel at most
+  // 10 K-blocks), and its k-rows start 16-byte aligned (N % 16 == 0 always; M % 16 for
+  // A stored [K][M])
+  const int64_t lim = (int64_t)1 << 31, kreach = small_k ? 10 * kKBlock : K;
+  if (layout_in_place(id) && (!a_t || (kreach * M < lim && M % 16 == 0)) &&
+      (!b_n || kreach * N < lim)) {
     maybe_print(kDense, M, N, K, 1, id);
     Problem p{};
     p.A = (const uint8_t*)A;

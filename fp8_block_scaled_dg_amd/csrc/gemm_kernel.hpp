@@ -109,6 +109,21 @@ __device__ __forceinline__ bool splitk_arrive(uint32_t* counter, uint32_t parts)
   return last;
 }
 
+// Operand memory layouts of the dense GEMM (bit set: the operand is stored with M or
+// N contiguous, i.e. as [K][M] or [K][N], instead of K-contiguous rows): the other
+// layouts of one GEMM family, C = op(A) op(B) with A stored [K][M] (T) and B stored
+// [K][N] (N) (DeepGEMM project page, aiproducthub.cn, "core features").
+constexpr int kLayAT = 1, kLayBN = 2;
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b8: in each group of 16 lanes, lanes 2j and 2j+1 address the two
+// 8-byte halves of 16 consecutive bytes of row j (j = 0..7), and lane i receives
+// byte i of each of those 8 rows -- an 8 x 16 byte block read transposed.
+__device__ __forceinline__ v2i tr8_at(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
+}
+
 // Bank-spreading swizzle of 16-byte chunks within a 128-byte LDS row.
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 

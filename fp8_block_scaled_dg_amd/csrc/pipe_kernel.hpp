@@ -113,12 +113,6 @@ __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, in
   tn = idx / gsize;
 }
 
-// Operand memory layouts of the dense GEMM (bit set: the operand is stored with M or
-// N contiguous, i.e. as [K][M] or [K][N], instead of K-contiguous rows): the other
-// layouts of one GEMM family, C = op(A) op(B) with A stored [K][M] (T) and B stored
-// [K][N] (N) (DeepGEMM project page, aiproducthub.cn, "core features").
-constexpr int kLayAT = 1, kLayBN = 2;
-
 // DMA sources of one thread: buffer resources for the tile's rows (wave-uniform,
 // SGPRs) plus 32-bit per-lane byte offsets; the K-block offset goes in the
 // instruction's scalar offset (a_kstep / b_kstep bytes per K-block: 128 for a
@@ -303,12 +297,6 @@ __device__ __forceinline__ void read_tile(const uint8_t* st, const uint32_t (&v)
   const uint8_t* p = st + tile * 32 * kKBlock;
   h0 = frag_at(p, v[0], v[1]);
   h1 = frag_at(p, v[2], v[3]);
-}
-
-typedef int v2i __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ v2i tr8_at(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p));
 }
 
 // The same fragments of an MN-contiguous operand staged as k-rows of ROW bytes: four

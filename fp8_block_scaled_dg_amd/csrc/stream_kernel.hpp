@@ -26,6 +26,19 @@
 // Loads past the unit's last K-block re-read that block (uniform wait counts); the
 // compute of such blocks is skipped. Rows past M or N clamp to the last row; such
 // outputs are never stored.
+//
+// Operands stored MN-contiguous (LAY bits, 64-column workgroups: W = 4, TN = 1), the
+// NN / TN / TT layouts of the DeepGEMM project page (aiproducthub.cn, "core
+// features"), are read in place. A K-block's tile of such an operand is 128 k-rows of
+// 64 bytes (the tile's 64 rows m or n), staged in LDS with chunk c of k-row k at
+// c ^ ((k >> 4) & 3), and each MFMA operand is gathered from it by four transposing
+// reads (ds_read_b64_tr_b8), each giving one row's 8 consecutive k:
+//   - A stored [K][M]: the block's A tile arrives by LDS DMA in that layout;
+//   - B stored [K][N]: each lane still loads two 16-byte k-row pieces per block into
+//     registers (so every load of the unit is in flight at once, as for B stored
+//     [N][K]). During block t the wave writes block t+1's pieces into a three-block
+//     LDS ring, so the writes overlap block t's work; the barrier of block t+1 makes
+//     them visible, and the transposing reads follow it.
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -52,6 +65,7 @@ template <int I>
 __shared__ __align__(16) uint8_t stream_a[64 * kKBlock];  // A tile of block I
 __shared__ __align__(16) uint8_t stream_sfa[3 * 1024];     // sfA: [group][row][4]
 __shared__ __align__(16) uint16_t stream_out[64 * 128];    // bf16 output staging
+__shared__ __align__(16) uint8_t stream_bt[3][128 * 64];   // B stored [K][N]: 3-block ring
 
 struct StreamArgs {
   Problem p;
@@ -68,6 +82,51 @@ struct StreamRegs {
   v4f sfb[Cfg::TN][Cfg::SF4];
 };
 
+// Operand sources of one lane: buffer resources at the unit's first K-block, per-lane
+// offsets, and the bytes one K-block advances (128 for K-contiguous rows, 128 x the
+// row length for an operand stored [K][M] or [K][N]); b_hi: from a lane's first B
+// piece to its second.
+template <class Cfg>
+struct StreamSrc {
+  __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc;
+  uint32_t a_off[Cfg::A_DMA];
+  uint32_t b_off[Cfg::TN];
+  uint32_t a_step, b_step, b_hi;
+};
+
+// MN-contiguous staging: byte offset of chunk c of k-row kr, and a lane's offset for
+// the transposing reads of the 16 rows 16c..16c+15 of the tile: lane (g, p) receives
+// row 16c + p at k in [16g, 16g + 16) and [64 + 16g, 80 + 16g), the k order of the
+// K-contiguous operands. In one read the 32 k-rows 16g + 8h + j (g = 0..3, j = 0..7)
+// fall on every 16-byte bank group exactly twice, since k mod 4 and the swizzle
+// (k >> 4) & 3 = g both vary.
+__device__ __forceinline__ uint32_t mn_lds_off(int kr, int c) {
+  return (uint32_t)(kr * 64 + ((c ^ ((kr >> 4) & 3)) << 4));
+}
+__device__ __forceinline__ uint32_t mn_read_off(int lane, int c) {
+  const int g = lane >> 4, p = lane & 15;
+  return (uint32_t)((16 * g + (p >> 1)) * 64 + ((c ^ g) << 4) + 8 * (p & 1));
+}
+__device__ __forceinline__ v8i mn_frag(const uint8_t* tile, uint32_t off) {
+  const uint8_t* q = tile + off;
+  const v2i a = tr8_at(q), b = tr8_at(q + 8 * 64), c = tr8_at(q + 64 * 64),
+            d = tr8_at(q + 72 * 64);
+  return v8i{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// A lane's LDS offsets for the MN-contiguous paths: where its two B pieces go
+// (bw0, bw1), and its transposing-read offsets for B (b_rd) and the four A row groups.
+struct StreamLane {
+  uint32_t bw0, bw1, b_rd;
+  uint32_t a_rd[4];
+};
+
+// A lane's two B pieces of one block (B stored [K][N]) into a ring slot.
+__device__ __forceinline__ void stream_ring_write(uint8_t* slot, const StreamLane& L, const v8i& v) {
+  *(v4u*)(slot + L.bw0) = v4u{(unsigned)v[0], (unsigned)v[1], (unsigned)v[2], (unsigned)v[3]};
+  *(v4u*)(slot + L.bw1) = v4u{(unsigned)v[4], (unsigned)v[5], (unsigned)v[6], (unsigned)v[7]};
+}
+
 // vmcnt = n, lgkmcnt = 0
 template <int n>
 __device__ __forceinline__ void stream_wait() {
@@ -76,23 +135,19 @@ __device__ __forceinline__ void stream_wait() {
 }
 
 template <class Cfg, int T>
-__device__ __forceinline__ void stream_issue_block(StreamRegs<Cfg>& r,
-                                                   __amdgpu_buffer_rsrc_t a_rsrc,
-                                                   const uint32_t (&a_off)[Cfg::A_DMA],
-                                                   __amdgpu_buffer_rsrc_t b_rsrc,
-                                                   const uint32_t (&b_off)[Cfg::TN], int tc,
-                                                   int wave) {
+__device__ __forceinline__ void stream_issue_block(StreamRegs<Cfg>& r, const StreamSrc<Cfg>& src,
+                                                   int tc, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const int koff = tc * kKBlock;
+  const uint32_t koa = (uint32_t)tc * src.a_step, kob = (uint32_t)tc * src.b_step;
 #pragma unroll
   for (int q = 0; q < Cfg::A_DMA; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        a_rsrc, (__attribute__((address_space(3))) void*)(stream_a<T> + (wave * Cfg::A_DMA + q) * 1024),
-        16, a_off[q], koff, 0, 0);
+        src.a_rsrc, (__attribute__((address_space(3))) void*)(stream_a<T> + (wave * Cfg::A_DMA + q) * 1024),
+        16, src.a_off[q], koa, 0, 0);
 #pragma unroll
   for (int j = 0; j < Cfg::TN; ++j) {
-    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[j], koff, 0);
-    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[j] + 64, koff, 0);
+    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(src.b_rsrc, src.b_off[j], kob, 0);
+    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(src.b_rsrc, src.b_off[j] + src.b_hi, kob, 0);
     r.b[T][j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
@@ -100,24 +155,33 @@ __device__ __forceinline__ void stream_issue_block(StreamRegs<Cfg>& r,
 }
 
 template <class Cfg, int T>
-__device__ __forceinline__ void stream_issue_all(StreamRegs<Cfg>& r, __amdgpu_buffer_rsrc_t a_rsrc,
-                                                 const uint32_t (&a_off)[Cfg::A_DMA],
-                                                 __amdgpu_buffer_rsrc_t b_rsrc,
-                                                 const uint32_t (&b_off)[Cfg::TN], int ks,
-                                                 int wave) {
+__device__ __forceinline__ void stream_issue_all(StreamRegs<Cfg>& r, const StreamSrc<Cfg>& src,
+                                                 int ks, int wave) {
   if constexpr (T < Cfg::D) {
-    stream_issue_block<Cfg, T>(r, a_rsrc, a_off, b_rsrc, b_off, T < ks ? T : ks - 1, wave);
-    stream_issue_all<Cfg, T + 1>(r, a_rsrc, a_off, b_rsrc, b_off, ks, wave);
+    stream_issue_block<Cfg, T>(r, src, T < ks ? T : ks - 1, wave);
+    stream_issue_all<Cfg, T + 1>(r, src, ks, wave);
   }
 }
 
-template <class Cfg, int T, bool PACKED>
+template <class Cfg, int T, bool PACKED, int LAY>
 __device__ __forceinline__ void stream_compute(v4f (&acc)[Cfg::TM][Cfg::TN], const StreamRegs<Cfg>& r,
-                                               int ks, int g, int l16, int shift) {
+                                               const StreamLane& L, int ks, int g, int l16,
+                                               int shift) {
   if constexpr (T < Cfg::D) {
     // this wave's loads of blocks 0..T have landed; every wave's A DMAs of block T
-    // are visible after the barrier
+    // are visible after the barrier. B stored [K][N]: block T's pieces were written
+    // into ring slot T % 3 during block T - 1 (block 0's here), and this wave's wait
+    // above (lgkmcnt 0) completed its writes before the barrier. Block T + 1's pieces
+    // go to slot (T + 1) % 3, last read in block T - 2: every wave finished those
+    // reads before it reached the barrier of block T - 1, which this wave has passed.
     stream_wait<(Cfg::D - 1 - T) * Cfg::OPB>();
+    if constexpr ((LAY & kLayBN) != 0) {
+      if (T == 0) {
+        stream_ring_write(stream_bt[0], L, r.b[0][0]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0, vmcnt and expcnt untouched
+      }
+      if (T + 1 < Cfg::D && T + 1 < ks) stream_ring_write(stream_bt[(T + 1) % 3], L, r.b[T + 1][0]);
+    }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (T < ks) {
@@ -127,32 +191,47 @@ __device__ __forceinline__ void stream_compute(v4f (&acc)[Cfg::TM][Cfg::TN], con
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int row = i * 16 + l16;
-        const uint8_t* rowp = stream_a<T> + row * kKBlock;
-        const v4u lo = *(const v4u*)(rowp + ((g ^ swz(row)) << 4));
-        const v4u hi = *(const v4u*)(rowp + (((g + 4) ^ swz(row)) << 4));
-        af[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        if constexpr ((LAY & kLayAT) != 0) {
+          af[i] = mn_frag(stream_a<T>, L.a_rd[i]);
+        } else {
+          const uint8_t* rowp = stream_a<T> + row * kKBlock;
+          const v4u lo = *(const v4u*)(rowp + ((g ^ swz(row)) << 4));
+          const v4u hi = *(const v4u*)(rowp + (((g + 4) ^ swz(row)) << 4));
+          af[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
         sa[i] = PACKED ? ue8m0_value(stream_sfa[row * 16 + shift + T])
                        : ((const float*)(stream_sfa + (T / 4) * 1024 + row * 16))[T % 4];
+      }
+      v8i bf[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr ((LAY & kLayBN) != 0)
+          bf[j] = mn_frag(stream_bt[T % 3], L.b_rd);
+        else
+          bf[j] = r.b[T][j];
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              r.b[T][j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+              bf[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
           const float s = sa[i] * r.sfb[j][T / 4][T % 4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(part[q], s, acc[i][j][q]);
         }
     }
-    stream_compute<Cfg, T + 1, PACKED>(acc, r, ks, g, l16, shift);
+    stream_compute<Cfg, T + 1, PACKED, LAY>(acc, r, L, ks, g, l16, shift);
   }
 }
 
 // PACKED: sfA in the packed UE8M0 layout (compile-time, as in the skinny kernel).
-template <class Cfg, bool PACKED>
+// LAY: kLayAT / kLayBN bits, the operands stored MN-contiguous.
+template <class Cfg, bool PACKED, int LAY = 0>
 __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
+  static_assert(LAY == 0 || (Cfg::W == 4 && Cfg::TN == 1),
+                "MN-contiguous operands: 64-column workgroups of 4 waves");
   constexpr int TN = Cfg::TN, TM = Cfg::TM, NT = Cfg::NT, BN = Cfg::BN;
   const Problem& p = args.p;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -172,23 +251,61 @@ __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
 
   // ---- sources: buffer resources over the unit's rows, 32-bit per-lane offsets
   const int a_rows = (int)(M < 64 ? M : 64);
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.A + (int64_t)kb0 * kKBlock), 0, 0x7FFFFFFF, 0x00020000);
-  uint32_t a_off[Cfg::A_DMA];
+  StreamSrc<Cfg> src;
+  StreamLane L{};
+  if constexpr ((LAY & kLayAT) != 0) {
+    // A stored [K][M] (M % 16 == 0): the DMA's 1 KB fills 16 k-rows of 64 bytes in
+    // order; lane l writes LDS chunk pc of its k-row, which holds chunk pc ^ swizzle;
+    // chunks past the last row m re-read the last valid one (never stored)
+    src.a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.A + (int64_t)kb0 * kKBlock * M), 0, 0x7FFFFFFF, 0x00020000);
+    src.a_step = (uint32_t)(kKBlock * M);
+    const int valid = (int)(M >> 4);
 #pragma unroll
-  for (int q = 0; q < Cfg::A_DMA; ++q) {
-    const int R = (wave * Cfg::A_DMA + q) * 8 + (lane >> 3), c = lane & 7;
-    const int row = R < a_rows ? R : a_rows - 1;
-    a_off[q] = (uint32_t)row * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+    for (int q = 0; q < Cfg::A_DMA; ++q) {
+      const int byte = (wave * Cfg::A_DMA + q) * 1024 + 16 * lane;
+      const int kr = byte >> 6, pc = (byte & 63) >> 4;
+      int lc = pc ^ ((kr >> 4) & 3);
+      if (lc >= valid) lc = valid - 1;
+      src.a_off[q] = (uint32_t)kr * (uint32_t)M + (uint32_t)(lc << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L.a_rd[i] = mn_read_off(lane, i);
+  } else {
+    src.a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.A + (int64_t)kb0 * kKBlock), 0, 0x7FFFFFFF, 0x00020000);
+    src.a_step = kKBlock;
+#pragma unroll
+    for (int q = 0; q < Cfg::A_DMA; ++q) {
+      const int R = (wave * Cfg::A_DMA + q) * 8 + (lane >> 3), c = lane & 7;
+      const int row = R < a_rows ? R : a_rows - 1;
+      src.a_off[q] = (uint32_t)row * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
+    }
   }
-  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.B + n0 * K + (int64_t)kb0 * kKBlock), 0, 0x7FFFFFFF, 0x00020000);
-  uint32_t b_off[TN];
+  if constexpr ((LAY & kLayBN) != 0) {
+    // B stored [K][N]: lane l loads 16 columns (chunk l % 4 of the tile, clamped to
+    // the last valid chunk) of k-rows 32 wave + l / 4 and 16 further
+    src.b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.B + (int64_t)kb0 * kKBlock * N + n0), 0, 0x7FFFFFFF, 0x00020000);
+    src.b_step = (uint32_t)(kKBlock * N);
+    src.b_hi = (uint32_t)(16 * N);
+    const int kr = wave * 32 + (lane >> 2), c = lane & 3;
+    const int valid = (int)((N - n0) >> 4);  // N % 16 == 0
+    src.b_off[0] = (uint32_t)kr * (uint32_t)N + (uint32_t)((c < valid ? c : valid - 1) << 4);
+    L.bw0 = mn_lds_off(kr, c);
+    L.bw1 = mn_lds_off(kr + 16, c);
+    L.b_rd = mn_read_off(lane, wave);
+  } else {
+    src.b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.B + n0 * K + (int64_t)kb0 * kKBlock), 0, 0x7FFFFFFF, 0x00020000);
+    src.b_step = kKBlock;
+    src.b_hi = 64;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    int64_t r = (wave * TN + j) * 16 + l16;
-    if (n0 + r >= N) r = N - 1 - n0;
-    b_off[j] = (uint32_t)r * (uint32_t)K + (uint32_t)(g * 16);
+    for (int j = 0; j < TN; ++j) {
+      int64_t r = (wave * TN + j) * 16 + l16;
+      if (n0 + r >= N) r = N - 1 - n0;
+      src.b_off[j] = (uint32_t)r * (uint32_t)K + (uint32_t)(g * 16);
+    }
   }
   // ---- issue every load of the unit
   StreamRegs<Cfg> r;
@@ -223,14 +340,14 @@ __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
     }
   }
 #endif
-  stream_issue_all<Cfg, 0>(r, a_rsrc, a_off, b_rsrc, b_off, ks, wave);
+  stream_issue_all<Cfg, 0>(r, src, ks, wave);
 
   v4f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  stream_compute<Cfg, 0, PACKED>(acc, r, ks, g, l16, kb0 & 3);
+  stream_compute<Cfg, 0, PACKED, LAY>(acc, r, L, ks, g, l16, kb0 & 3);
 
   // ---- split reduction. Partials are written and read with device-scope (sc1)
   // 16-byte accesses (measured faster here than L2-resident ones); splitk_arrive

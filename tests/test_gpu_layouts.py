@@ -4,12 +4,13 @@ on integer-valued inputs and within the tolerance on N(0,1) inputs; and each cal
 must equal dg_fp8_gemm_nt on transposed copies of its operands bit for bit, up to the
 full prefill shape.
 
-Two paths serve these calls. Shapes of the compute-bound kernel (M > 64) read the
-[K][M] / [K][N] operands in place (k-row tiles, transposing LDS reads): covered on
-both tile shapes, M and N tails, the dense tail split, long K, and by capture into a
-HIP graph on a fresh stream, which succeeds only because nothing is allocated. M <= 64
-and A stored [K][M] with M % 16 != 0 go through a transposed copy: odd M, M = 1 and the
-decode kernels cover that path."""
+Two paths serve these calls. Shapes of the compute-bound kernel (M > 64) and of the
+M <= 64 stream kernel read the [K][M] / [K][N] operands in place (k-row tiles,
+transposing LDS reads): covered on both compute-bound tile shapes and both stream
+configurations, M and N tails, the dense tail split, split K, long K, and by capture
+into a HIP graph on a fresh stream, which succeeds only because nothing is allocated.
+A stored [K][M] with M % 16 != 0, and the M <= 64 shapes of the rolling kernel, go
+through a transposed copy: odd M, M = 1 and short K cover that path."""
 import numpy as np
 import pytest
 import torch
@@ -126,3 +127,36 @@ def test_native_layout_allocates_nothing(layout):
         torch.cuda.synchronize()
         got = c.view(torch.int16).cpu().numpy().view(np.uint16)
         assert_bitwise(got, oracle.gemm(A, B, sfA, sfB, layout), what=f"{layout} replay {rep}")
+
+
+STREAM_MN = [(64, 2112, 7168), (64, 2112, 2048), (16, 272, 2560), (48, 80, 1280),
+             (37, 96, 1536), (64, 32768, 512), (1, 16, 128)]
+
+
+@pytest.mark.parametrize("cfg", ["stream_w4_tn1_d10", "stream_w4_tn1_d4"])
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_stream_layouts_bitwise(cfg, layout, monkeypatch):
+    """M <= 64 on the stream kernel: B stored [K][N] staged through the LDS ring, A
+    stored [K][M] (M % 16 == 0) by DMA, both read transposed; the decode shape with its
+    6-way split K, split K on short K, column tails of 16 and 32, M = 1, 16, 37, 48
+    (37: A stored [K][M] takes the copy path), one K-block. A configuration whose K run
+    does not fit a shape falls back to the default choice (64x2112x7168 on the 4-block
+    one)."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    for (M, N, K) in STREAM_MN:
+        rng = np.random.default_rng(M + 5 * N + 3 * K + ord(layout[0]) + 7 * ord(layout[1]))
+        A_mk, B_nk, sfA, sfB = int_operands(rng, M, N, K)
+        A, B = stored(A_mk, B_nk, layout)
+        g = run(layout, A, B, sfA, sfB, M, N)
+        assert_bitwise(g, oracle.gemm(A, B, sfA, sfB, layout), what=f"{cfg} {layout} {M}x{N}x{K}")
+        assert np.array_equal(g, run("nt", A_mk, B_nk, sfA, sfB, M, N))
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_decode_layout_gaussian(layout):
+    M, N, K = 64, 2112, 7168
+    w = synth.dense(M, N, K, 780000)
+    A, B = stored(w.A, w.B, layout)
+    g = run(layout, A, B, w.sfA, w.sfB, M, N)
+    print(layout, assert_parity(g, oracle.gemm(A, B, w.sfA, w.sfB, layout), what=layout))
+    assert np.array_equal(g, run("nt", w.A, w.B, w.sfA, w.sfB, M, N))
