@@ -837,6 +837,9 @@ def _csv_rows(folder: str, suffix: str):
         return list(csv.DictReader(f))
 
 
+PROBE_KERNELS = ("stream_read_kernel", "mfma_rate_kernel", "empty_kernel")
+
+
 def _ours(name: str) -> bool:
     return "dg::" in name
 
@@ -973,6 +976,36 @@ def summarize(manifest_path: str) -> None:
             span = (last[-1][1] - last[0][0]) / len(last) / 1e3
             lines.append(f"| `{k}` | {len(last)} | {avg:.2f} | {span:.2f} |")
             timed.setdefault(t["label"], {})[k] = avg
+        probes = {}
+        for r in _csv_rows(t["dir"], "kernel_trace.csv"):
+            name = r["Kernel_Name"]
+            tag = next((p for p in PROBE_KERNELS if p in name), None)
+            if tag is None:
+                continue
+            if "<true>" in name:
+                tag += " (non-temporal)"
+            wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            probes.setdefault((tag, wgs), []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        if probes:
+            # the streaming reads run byte count by byte count (outer loop), in the order
+            # of the line's hbm_ceiling entries
+            sizes = [int(k) for k in (line.get("hbm_ceiling") or {}) if k.isdigit()]
+            lines += ["", "Calibration probes of the same run (libdg_probe.so), kernel time; "
+                          "bench.py graph-times them itself and reports the best streaming-read "
+                          "configuration per byte count:", "",
+                      "| probe | bytes | workgroups | dispatches | min us | median us |",
+                      "|---|---|---|---|---|---|"]
+            for (tag, wgs), d in sorted(probes.items()):
+                d.sort()
+                parts = [(None, d)]
+                if tag.startswith("stream_read") and sizes and len(d) % len(sizes) == 0:
+                    n = len(d) // len(sizes)
+                    parts = [(sizes[i], d[i * n:(i + 1) * n]) for i in range(len(sizes))]
+                for nbytes, seg in parts:
+                    us = sorted((e - s0) / 1e3 for s0, e in seg)
+                    lines.append(f"| `{tag}` | {nbytes or ''} | {wgs} | {len(us)} | "
+                                 f"{us[0]:.2f} | {us[len(us) // 2]:.2f} |")
         lines += ["", "bench.py line of the same run (HIP events around each GEMM's "
                       "back-to-back launches):", ""]
         for k in line["kernels"]:

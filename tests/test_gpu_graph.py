@@ -2,7 +2,8 @@
 same shapes already ran, replayed several times with eager work and synchronisations
 in between; every replay must reproduce the eager result bit for bit. Covered: the
 split-K decode kernel (its arrival counters must be back at zero after every launch),
-the compute-bound kernel's split tail, and the masked grouped call. The library
+also reading B stored [K][N] and A stored [K][M] in place, the compute-bound kernel's
+split tail, and the masked grouped call. The library
 allocates nothing for a shape it has run on the stream before, so nothing but the
 kernels is recorded."""
 import numpy as np
@@ -28,6 +29,18 @@ def _dense(M, N, K, seed):
     return (lambda: dg().fp8_gemm_nt(a, b, c, sa, sb)), c
 
 
+def _layout(layout, M, N, K, seed):
+    """A stored [K][M] for layout[0] == 't', B stored [K][N] for layout[1] == 'n'."""
+    rng = np.random.default_rng(seed)
+    A, B, sfA, sfB = int_operands(rng, M, N, K)
+    A = np.ascontiguousarray(A.T) if layout[0] == "t" else A
+    B = np.ascontiguousarray(B.T) if layout[1] == "n" else B
+    a, b, sa, sb = gu.codes(A), gu.codes(B), gu.dev(sfA), gu.dev(sfB)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    call = getattr(dg(), "fp8_gemm_" + layout)
+    return (lambda: call(a, b, c, sa, sb)), c
+
+
 def _masked(seed):
     rng = np.random.default_rng(seed)
     G, M_max, N, K = 6, 200, 512, 1024
@@ -41,10 +54,15 @@ def _masked(seed):
     return (lambda: dg().m_grouped_fp8_gemm_nt_masked(a, b, c, sa, sb, mm)), c
 
 
-@pytest.mark.parametrize("case", ["decode_splitk", "dense_tail_split", "masked"])
+@pytest.mark.parametrize("case", ["decode_splitk", "dense_tail_split", "masked",
+                                  "decode_nn_in_place", "decode_tn_in_place"])
 def test_graph_replays_match_eager(case):
     if case == "decode_splitk":
         fn, c = _dense(64, 2112, 7168, 5)
+    elif case == "decode_nn_in_place":
+        fn, c = _layout("nn", 64, 2112, 7168, 8)
+    elif case == "decode_tn_in_place":
+        fn, c = _layout("tn", 48, 1040, 4096, 9)
     elif case == "dense_tail_split":
         fn, c = _dense(384, 768, 2048, 6)
     else:
