@@ -640,7 +640,8 @@ def main():
                     "to bf16", "output": "e4m3fn codes + fp32 power-of-two scale per 1x128",
                     "parallelism": "single GPU", "rotation_copies": copies, "timing": args.timing}
                    if args.workload == "quant" else
-                   {"workload": DESCRIPTIONS[args.workload], "inputs": "seeded N(0,1) quantized to "
+                   {"workload": DESCRIPTIONS[args.workload].replace(" NT ", f" {args.layout.upper()} "),
+                    "inputs": "seeded N(0,1) quantized to "
                     "e4m3fn, A per 1x128, B per 128x128, power-of-two scales",
                     "sfa_layout": "packed UE8M0" if args.sfa == "ue8m0" else "fp32",
                     "operand_layout": args.layout.upper(),
@@ -822,7 +823,10 @@ def measured_traffic(kernel_name: str, build_id: str):
 #    "traffic": {"calibration": {"fetch": DIR, "write": DIR, "command_fetch": ...,
 #                                "command_write": ...},
 #                "gemms": [{"gemm": "dec2112", "workload": "decode", "fetch": DIR,
-#                           "write": DIR, "command_fetch": ..., "command_write": ...}]}}
+#                           "write": DIR, "command_fetch": ..., "command_write": ...,
+#                           "bench_fetch": OUT, "bench_write": OUT}]}}
+# (bench_fetch / bench_write: the counter runs' stdout, whose bench line names the
+# library build the counters were taken on)
 # and --summarize turns them into short text summaries under profiles/.
 
 def _csv_rows(folder: str, suffix: str):
@@ -938,6 +942,46 @@ def _summarize_operand_path(passes, out_dir: str) -> None:
         f.write("\n".join(md) + "\n")
 
 
+INSTMIX = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_LDS",
+           "SQ_INSTS_VMEM", "SQ_INSTS_SALU", "SQ_INSTS_VALU_MFMA_F8", "SQ_INSTS_VALU_MFMA_F6F4")
+
+
+def _summarize_instmix(entries, out_dir: str) -> None:
+    """Wave-instruction mix of our kernel per workload (SQ_INSTS_*: each wave
+    instruction counted once, summed over the GPU), averaged over its dispatches. The
+    promotion is one fp32 FMA per accumulator element and K-block, i.e. M_v * N * KB / 64
+    wave instructions; the table sets the FMAs counted against that and against the
+    MFMAs (MFMA counts VALU-class instructions too: the other VALU is VALU - MFMA - FMA)."""
+    md = ["# Instruction mix (rocprofv3 SQ_INSTS_*)", "",
+          "Wave instructions per launch of our kernel (one count per wave instruction, summed "
+          "over every wave), averaged over its dispatches. Promotion FMAs: the algorithmic count "
+          "is one fp32 FMA per output element and K-block, M_v x N x K/128 / 64 wave "
+          "instructions.", "",
+          "| workload | MFMA | fp32 FMA | promotion FMAs (algorithmic) | FMA per MFMA | other VALU | "
+          "LDS | VMEM | SALU |", "|---|---|---|---|---|---|---|---|---|"]
+    for e in entries:
+        v = {c: _per_dispatch(e["dir"], c)[0] for c in INSTMIX}
+        ks = [k for k in v["SQ_INSTS_MFMA"] if _ours(k)]
+        if len(ks) != 1:
+            raise RuntimeError(f"{e['label']}: expected one of our kernels, got {ks}")
+        k = ks[0]
+        g = {c: v[c].get(k, 0.0) for c in INSTMIX}
+        bj = e["dir"] + ".json"
+        bj = bj if os.path.isabs(bj) else os.path.join(ROOT, bj)
+        with open(bj) as f:
+            line = json.loads([x for x in f.read().splitlines() if x.startswith("{")][-1])
+        alg = sum(kk["alg_flops"] / 2 / 128 / 64 for kk in line["kernels"])
+        mfma = g["SQ_INSTS_MFMA"]
+        other = g["SQ_INSTS_VALU"] - mfma - g["SQ_INSTS_VALU_FMA_F32"]
+        md.append(f"| {e['label']} | {mfma:.4g} | {g['SQ_INSTS_VALU_FMA_F32']:.4g} | {alg:.4g} | "
+                  f"{g['SQ_INSTS_VALU_FMA_F32'] / max(mfma, 1):.2f} | {other:.4g} | "
+                  f"{g['SQ_INSTS_LDS']:.4g} | {g['SQ_INSTS_VMEM']:.4g} | {g['SQ_INSTS_SALU']:.4g} |")
+    md += ["", "Commands (repository root on the GPU host):", ""]
+    md += ["    " + e["command"] for e in entries]
+    with open(os.path.join(out_dir, "counters_instmix.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
 def summarize(manifest_path: str) -> None:
     with open(manifest_path) as f:
         man = json.load(f)
@@ -968,13 +1012,15 @@ def summarize(manifest_path: str) -> None:
         lines += ["", f"Kernel trace of the timed region only (each kernel's last {K} "
                       "dispatches); `span` is first start to last end over the dispatches, "
                       "the launch-to-launch time:", "",
-                  "| kernel | dispatches | avg us | span us per dispatch |", "|---|---|---|---|"]
+                  "| kernel | dispatches | avg us | median us | span us per dispatch |",
+                  "|---|---|---|---|---|"]
         for k, ts in per.items():
             ts.sort()
             last = ts[-K:]
             avg = sum(e - s for s, e in last) / len(last) / 1e3
+            med = sorted(e - s for s, e in last)[len(last) // 2] / 1e3
             span = (last[-1][1] - last[0][0]) / len(last) / 1e3
-            lines.append(f"| `{k}` | {len(last)} | {avg:.2f} | {span:.2f} |")
+            lines.append(f"| `{k}` | {len(last)} | {avg:.2f} | {med:.2f} | {span:.2f} |")
             timed.setdefault(t["label"], {})[k] = avg
         probes = {}
         for r in _csv_rows(t["dir"], "kernel_trace.csv"):
@@ -1020,6 +1066,9 @@ def summarize(manifest_path: str) -> None:
     ps = man.get("passes")
     if ps:
         _summarize_operand_path(ps, out_dir)
+    im = man.get("instmix")
+    if im:
+        _summarize_instmix(im, out_dir)
     tr = man.get("traffic")
     if tr:
         cal = tr["calibration"]
@@ -1034,8 +1083,18 @@ def summarize(manifest_path: str) -> None:
         kern = k_f[1]
         f_scale = copy_kib / cf[kern]
         w_scale = copy_kib / cw[kern]
-        import fp8_block_scaled_dg_amd as dgb  # the library build the counters were taken on
-        rec = {"build_id": dgb.BUILD_ID,
+        # the library build the counters were taken on: the build id on the bench lines of
+        # the counter runs themselves (every run must agree)
+        ids = set()
+        for g in tr["gemms"]:
+            for key in ("bench_fetch", "bench_write"):
+                bj = g[key] if os.path.isabs(g[key]) else os.path.join(ROOT, g[key])
+                with open(bj) as f:
+                    ids.add(json.loads([x for x in f.read().splitlines()
+                                        if x.startswith("{")][-1])["build_id"])
+        if len(ids) != 1:
+            raise RuntimeError(f"counter runs on different library builds: {sorted(ids)}")
+        rec = {"build_id": ids.pop(),
                "calibration": {"kernel": _short(kern), "copy_bytes": copy_kib * 1024,
                                "fetch_kib": cf[kern], "write_kib": cw[kern],
                                "fetch_scale": f_scale, "write_scale": w_scale,
