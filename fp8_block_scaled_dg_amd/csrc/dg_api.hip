@@ -361,15 +361,39 @@ dg_status launch_skinny(const Problem& p0, int64_t blocks, hipStream_t stream) {
 // Split choice of the stream kernel: all splits of a column tile share an XCD, so an
 // XCD holds ceil(tiles / 8) tiles times S splits and should not exceed its 32 CUs.
 struct StreamPlan {
-  int64_t tiles, S, KS, grid;
+  int64_t tiles, S, KS, grid, group;
 };
 
-template <class Cfg>
+// Most column tiles one XCD holds when groups of G consecutive tiles go to the XCDs
+// round robin (group q on XCD q % 8; the last group may be short); the kernel gives an
+// XCD's tiles the slots 0, 1, ... in group order. G = 1: ceil(tiles / 8).
+int64_t stream_tiles_per_xcd(int64_t tiles, int G) {
+  int64_t most = 0;
+  for (int64_t x = 0; x < 8; ++x) {
+    int64_t n = 0;
+    for (int64_t q = x; q * G < tiles; q += 8) n += tiles - q * G < G ? tiles - q * G : G;
+    most = n > most ? n : most;
+  }
+  return most;
+}
+
+// LAY with kLayBN (B stored [K][N]): column tiles go to the XCDs in groups of 4 or 2
+// consecutive ones (the kernel's mapping explains why), the largest group that leaves
+// the most tiles per XCD, and so the split, as they are with single tiles.
+template <class Cfg, int LAY = 0>
 StreamPlan stream_plan(int64_t N, int64_t K) {
   StreamPlan pl;
   const int64_t KB = K / kKBlock;
   pl.tiles = (N + Cfg::BN - 1) / Cfg::BN;
-  const int64_t per_xcd = (pl.tiles + 7) / 8;
+  const int64_t per_xcd = stream_tiles_per_xcd(pl.tiles, 1);
+  pl.group = 1;
+  if (LAY & kLayBN) {
+    for (int G : {4, 2})
+      if (stream_tiles_per_xcd(pl.tiles, G) == per_xcd) {
+        pl.group = G;
+        break;
+      }
+  }
   int64_t S = (kCUs / 8) / per_xcd;
   if (S > Cfg::SMAX) S = Cfg::SMAX;
   if (S > KB) S = KB;
@@ -390,13 +414,14 @@ template <class Cfg, int LAY = 0>
 dg_status launch_stream(const Problem& p0, int64_t blocks, hipStream_t stream) {
   (void)blocks;
   if (LAY != 0 && p0.sfa_packed) return fail(DG_ERR_UNSUPPORTED_SHAPE, "packed sfA with MN-contiguous operands");
-  const StreamPlan pl = stream_plan<Cfg>(p0.N, p0.K);
+  const StreamPlan pl = stream_plan<Cfg, LAY>(p0.N, p0.K);
   if (pl.KS > Cfg::D) return fail(DG_ERR_UNSUPPORTED_SHAPE, "K run %lld > %d", (long long)pl.KS, Cfg::D);
   StreamArgs a{};
   a.p = p0;
   a.S = (int32_t)pl.S;
   a.KS = (int32_t)pl.KS;
   a.tiles = (int32_t)pl.tiles;
+  a.group = (int32_t)pl.group;
   if (pl.grid > 0x7FFFFFFF) return fail(DG_ERR_UNSUPPORTED_SHAPE, "grid of %lld", (long long)pl.grid);
   if (pl.S > 1) {
     const size_t part = (size_t)(pl.tiles * pl.S) * 64 * Cfg::BN * sizeof(float);
@@ -859,6 +884,8 @@ dg_status launch_layout(int id, const Problem& p, hipStream_t st) {
   return launch_pipe<Pipe128x256, kDense, LAY>(p, 1, st);
 }
 
+// The configuration reads MN-contiguous operands in place: the compute-bound kernels
+// and the 64-column stream kernels.
 bool layout_in_place(int id) {
   const char* name = kTable[id].name;
   return strncmp(name, "pipe", 4) == 0 || strcmp(name, "stream_w4_tn1_d10") == 0 ||

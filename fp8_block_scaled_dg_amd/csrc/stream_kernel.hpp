@@ -74,6 +74,7 @@ struct StreamArgs {
   int32_t S;           // K splits
   int32_t KS;          // K-blocks per split (the last split may have fewer)
   int32_t tiles;
+  int32_t group;       // consecutive column tiles per XCD group (workgroup mapping)
 };
 
 template <class Cfg>
@@ -241,9 +242,16 @@ __global__ void __launch_bounds__(Cfg::NT) stream_kernel(StreamArgs args) {
   const int KB = (int)(K / kKBlock);
   const int S = args.S;
 
-  // workgroup -> (tile, split): tile t's splits all run on XCD t % 8
+  // workgroup -> (tile, split): the column tiles are dealt to the XCDs in groups of G
+  // consecutive ones, group q on XCD q % 8, and all splits of a tile run on its XCD.
+  // G = 1 for B stored [N][K]. With B stored [K][N] a tile's k-row piece is 64 bytes,
+  // half of a 128-byte cache line shared with a neighbouring tile (which one alternates
+  // with the k-row when N % 128 == 64), so G up to 4 keeps both on one XCD, whose L2
+  // then fetches the line once, except across the edges of a group.
+  const int G = args.group;
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-  const int tile = (local / S) * 8 + xcd, split = local - (local / S) * S;
+  const int slot = local / S, split = local - slot * S;
+  const int tile = ((slot / G) * 8 + xcd) * G + slot % G;
   if (tile >= args.tiles) return;
   const int64_t n0 = (int64_t)tile * BN;
   const int kb0 = split * args.KS;

@@ -130,7 +130,8 @@ def test_native_layout_allocates_nothing(layout):
 
 
 STREAM_MN = [(64, 2112, 7168), (64, 2112, 2048), (16, 272, 2560), (48, 80, 1280),
-             (37, 96, 1536), (64, 32768, 512), (1, 16, 128)]
+             (37, 96, 1536), (64, 32768, 512), (1, 16, 128), (32, 1072, 4096),
+             (64, 2560, 2048)]
 
 
 @pytest.mark.parametrize("cfg", ["stream_w4_tn1_d10", "stream_w4_tn1_d4"])
@@ -138,10 +139,11 @@ STREAM_MN = [(64, 2112, 7168), (64, 2112, 2048), (16, 272, 2560), (48, 80, 1280)
 def test_stream_layouts_bitwise(cfg, layout, monkeypatch):
     """M <= 64 on the stream kernel: B stored [K][N] staged through the LDS ring, A
     stored [K][M] (M % 16 == 0) by DMA, both read transposed; the decode shape with its
-    6-way split K, split K on short K, column tails of 16 and 32, M = 1, 16, 37, 48
-    (37: A stored [K][M] takes the copy path), one K-block. A configuration whose K run
-    does not fit a shape falls back to the default choice (64x2112x7168 on the 4-block
-    one)."""
+    6-way split K, split K on short K, column tails of 16, 32 and 48, M = 1, 16, 37, 48
+    (37: A stored [K][M] takes the copy path), one K-block; column tiles dealt to the
+    XCDs in groups of 4 (2112 and 32768 columns), 2 (1072) and 1 (2560, 272). A
+    configuration whose K run does not fit a shape falls back to the default choice
+    (64x2112x7168 on the 4-block one)."""
     monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
     for (M, N, K) in STREAM_MN:
         rng = np.random.default_rng(M + 5 * N + 3 * K + ord(layout[0]) + 7 * ord(layout[1]))
