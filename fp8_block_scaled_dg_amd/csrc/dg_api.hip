@@ -307,17 +307,46 @@ dg_status launch_transpose(const uint8_t* src, uint8_t* dst, int64_t R, int64_t 
   return err == hipSuccess ? DG_OK : fail(DG_ERR_LAUNCH, "transpose: %s", hipGetErrorString(err));
 }
 
-template <class Cfg>
+// Most column tiles one XCD holds when groups of G consecutive tiles go to the XCDs
+// round robin (group q on XCD q % 8; the last group may be short); the kernel gives an
+// XCD's tiles the slots 0, 1, ... in group order. G = 1: ceil(tiles / 8).
+int64_t tiles_per_xcd(int64_t tiles, int G) {
+  int64_t most = 0;
+  for (int64_t x = 0; x < 8; ++x) {
+    int64_t n = 0;
+    for (int64_t q = x; q * G < tiles; q += 8) n += tiles - q * G < G ? tiles - q * G : G;
+    most = n > most ? n : most;
+  }
+  return most;
+}
+
+// LAY with kLayBN (B stored [K][N]): column tiles go to the XCDs in groups of 4 or 2
+// consecutive ones (the kernel's mapping explains why), the largest group that leaves
+// the most tiles per XCD, and so the split, as they are with single tiles.
+// B stored [K][N] on the M <= 64 kernels: a 64-column tile's k-row piece is half a
+// 128-byte line shared with a neighbouring tile, so column tiles go to the XCDs in
+// groups of consecutive ones: the largest group of 4 or 2 that leaves the most tiles
+// per XCD as with single tiles (so the split is unchanged), else 1.
+int tile_group(int64_t tiles) {
+  const int64_t one = tiles_per_xcd(tiles, 1);
+  for (int G : {4, 2})
+    if (tiles_per_xcd(tiles, G) == one) return G;
+  return 1;
+}
+
+template <class Cfg, int LAY = 0>
 dg_status launch_skinny(const Problem& p0, int64_t blocks, hipStream_t stream) {
   (void)blocks;
+  if (LAY != 0 && p0.sfa_packed) return fail(DG_ERR_UNSUPPORTED_SHAPE, "packed sfA with MN-contiguous operands");
+  constexpr int lds_bytes = (LAY & kLayBN) ? Cfg::LDS_BYTES_BN : Cfg::LDS_BYTES;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
-    attr_err = hipFuncSetAttribute((const void*)skinny_kernel<Cfg, false>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
-    if (attr_err == hipSuccess)
+    attr_err = hipFuncSetAttribute((const void*)skinny_kernel<Cfg, false, LAY>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (attr_err == hipSuccess && LAY == 0)
       attr_err = hipFuncSetAttribute((const void*)skinny_kernel<Cfg, true>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   });
   if (attr_err != hipSuccess)
     return fail(DG_ERR_LAUNCH, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
@@ -338,19 +367,26 @@ dg_status launch_skinny(const Problem& p0, int64_t blocks, hipStream_t stream) {
   a.KS = KS;
   a.p.tiles_m = 1;
   a.p.tiles_n = (int32_t)tiles;
-  const int64_t grid = tiles * S;
+  a.tiles = (int32_t)tiles;
+  // B stored [K][N]: workgroups are dealt to the XCDs (workgroup b on XCD b % 8), so the
+  // grid covers every XCD's most tiles; the kernel leaves idle slots at once
+  a.group = (LAY & kLayBN) ? tile_group(tiles) : 1;
+  const int64_t grid = (LAY & kLayBN) ? 8 * tiles_per_xcd(tiles, 1) * S : tiles * S;
   if (grid > 0x7FFFFFFF) return fail(DG_ERR_UNSUPPORTED_SHAPE, "grid of %lld", (long long)grid);
   if (S > 1) {
-    const size_t part = (size_t)grid * 64 * Cfg::BN * sizeof(float);
+    const size_t part = (size_t)(tiles * S) * 64 * Cfg::BN * sizeof(float);
     dg_status st = get_workspace(stream, part, (size_t)tiles, &a.ws, &a.counters);
     if (st != DG_OK) return st;
   }
-  if (p0.sfa_packed)
+  if (LAY != 0)
+    hipLaunchKernelGGL((skinny_kernel<Cfg, false, LAY>), dim3((unsigned)grid), dim3(Cfg::NT),
+                       lds_bytes, stream, a);
+  else if (p0.sfa_packed)
     hipLaunchKernelGGL((skinny_kernel<Cfg, true>), dim3((unsigned)grid), dim3(Cfg::NT),
-                       Cfg::LDS_BYTES, stream, a);
+                       lds_bytes, stream, a);
   else
     hipLaunchKernelGGL((skinny_kernel<Cfg, false>), dim3((unsigned)grid), dim3(Cfg::NT),
-                       Cfg::LDS_BYTES, stream, a);
+                       lds_bytes, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
   return DG_OK;
@@ -364,36 +400,13 @@ struct StreamPlan {
   int64_t tiles, S, KS, grid, group;
 };
 
-// Most column tiles one XCD holds when groups of G consecutive tiles go to the XCDs
-// round robin (group q on XCD q % 8; the last group may be short); the kernel gives an
-// XCD's tiles the slots 0, 1, ... in group order. G = 1: ceil(tiles / 8).
-int64_t stream_tiles_per_xcd(int64_t tiles, int G) {
-  int64_t most = 0;
-  for (int64_t x = 0; x < 8; ++x) {
-    int64_t n = 0;
-    for (int64_t q = x; q * G < tiles; q += 8) n += tiles - q * G < G ? tiles - q * G : G;
-    most = n > most ? n : most;
-  }
-  return most;
-}
-
-// LAY with kLayBN (B stored [K][N]): column tiles go to the XCDs in groups of 4 or 2
-// consecutive ones (the kernel's mapping explains why), the largest group that leaves
-// the most tiles per XCD, and so the split, as they are with single tiles.
 template <class Cfg, int LAY = 0>
 StreamPlan stream_plan(int64_t N, int64_t K) {
   StreamPlan pl;
   const int64_t KB = K / kKBlock;
   pl.tiles = (N + Cfg::BN - 1) / Cfg::BN;
-  const int64_t per_xcd = stream_tiles_per_xcd(pl.tiles, 1);
-  pl.group = 1;
-  if (LAY & kLayBN) {
-    for (int G : {4, 2})
-      if (stream_tiles_per_xcd(pl.tiles, G) == per_xcd) {
-        pl.group = G;
-        break;
-      }
-  }
+  const int64_t per_xcd = tiles_per_xcd(pl.tiles, 1);
+  pl.group = (LAY & kLayBN) ? tile_group(pl.tiles) : 1;
   int64_t S = (kCUs / 8) / per_xcd;
   if (S > Cfg::SMAX) S = Cfg::SMAX;
   if (S > KB) S = KB;
@@ -868,28 +881,31 @@ dg_status dg_m_grouped_fp8_gemm_nt_masked_swiglu(const void* A, const void* B, v
 namespace dg {
 namespace {
 
-// C = op(A) op(B) with A stored [K][M] (a_t) and/or B stored [K][N] (b_n). Shapes the
-// compute-bound kernel or the split-K decode kernel serves read such operands in
-// place: their tiles are staged as k-rows and transposed on the way from LDS into the
-// MFMA (kLayAT / kLayBN). The other kernels (the rolling M <= 64 kernel, the tiled
-// kernel past the compute-bound kernel's K range) take K-contiguous operands only:
-// there the operand is first transposed into the stream's workspace and the NT
-// kernels run on the copy.
+// C = op(A) op(B) with A stored [K][M] (a_t) and/or B stored [K][N] (b_n). The
+// compute-bound kernel and the M <= 64 kernels read such operands in place: their tiles
+// are staged as k-rows and transposed on the way from LDS into the MFMA (kLayAT /
+// kLayBN). The tiled kernel past the compute-bound kernel's K range, and A stored
+// [K][M] with M % 16 != 0, take the other route: the operand is first transposed into
+// the stream's workspace and the NT kernels run on the copy.
 template <int LAY>
 dg_status launch_layout(int id, const Problem& p, hipStream_t st) {
   const char* name = kTable[id].name;
   if (strcmp(name, "stream_w4_tn1_d10") == 0) return launch_stream<Stream1x10, LAY>(p, 1, st);
   if (strcmp(name, "stream_w4_tn1_d4") == 0) return launch_stream<Stream1x4, LAY>(p, 1, st);
+  if (strcmp(name, "skinny_w4_tn1_d2") == 0) return launch_skinny<SkinnyCfg<4, 1, 2>, LAY>(p, 1, st);
+  if (strcmp(name, "skinny_w4_tn1_d3") == 0) return launch_skinny<SkinnyCfg<4, 1, 3>, LAY>(p, 1, st);
+  if (strcmp(name, "skinny_w4_tn1_d5") == 0) return launch_skinny<SkinnyCfg<4, 1, 5>, LAY>(p, 1, st);
+  if (strcmp(name, "skinny_w4_tn1_d8") == 0) return launch_skinny<SkinnyCfg<4, 1, 8>, LAY>(p, 1, st);
   if (strcmp(name, "pipe256x128") == 0) return launch_pipe<Pipe256x128, kDense, LAY>(p, 1, st);
   return launch_pipe<Pipe128x256, kDense, LAY>(p, 1, st);
 }
 
 // The configuration reads MN-contiguous operands in place: the compute-bound kernels
-// and the 64-column stream kernels.
+// and the 64-column, 4-wave M <= 64 kernels.
 bool layout_in_place(int id) {
   const char* name = kTable[id].name;
-  return strncmp(name, "pipe", 4) == 0 || strcmp(name, "stream_w4_tn1_d10") == 0 ||
-         strcmp(name, "stream_w4_tn1_d4") == 0;
+  return strncmp(name, "pipe", 4) == 0 || strncmp(name, "stream_w4_tn1_", 14) == 0 ||
+         strncmp(name, "skinny_w4_tn1_", 14) == 0;
 }
 
 dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
@@ -901,20 +917,18 @@ dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
   if (s != DG_OK || M == 0 || N == 0) return s;
   if (M > (int64_t)1 << 30) return fail(DG_ERR_UNSUPPORTED_SHAPE, "M beyond 2^30");
   const hipStream_t st = (hipStream_t)stream;
-  int id = select_config(kDense, M, M, N, K, 1);
-  // M <= 64 with B stored [K][N] and at most 8 K-blocks: the 128x256-tile kernel in
-  // place beats both transposing B for the rolling kernel and the split-K decode
-  // kernel in place (64x32768x512 NN: 11.5 against 16.5 and 15.0 us); with long K the
-  // decode kernel in place wins (64x2112x7168 NN: 13.1 against 21.1 us copied and
-  // 24.6 us on the 128x256-tile kernel)
-  const char* forced = getenv("DG_FORCE_CONFIG");
-  if (M <= 64 && b_n && K / kKBlock <= 8 && !(forced && *forced)) id = find_cfg("pipe128x256");
-  const bool small_k = strncmp(kTable[id].name, "stream", 6) == 0;
+  // the NT call's configuration: every M <= 64 kernel it picks reads these layouts in
+  // place too (64x32768x512 NN on the rolling kernel: 9.5 us, against 12.9 us on the
+  // 128x256-tile kernel and 16.5 us through a copy)
+  const int id = select_config(kDense, M, M, N, K, 1);
   // in place: 32-bit buffer offsets reach every byte of an MN-contiguous operand (the
-  // compute-bound kernel addresses all of K from one base, the M <= 64 kernel at most
-  // 10 K-blocks), and its k-rows start 16-byte aligned (N % 16 == 0 always; M % 16 for
-  // A stored [K][M])
-  const int64_t lim = (int64_t)1 << 31, kreach = small_k ? 10 * kKBlock : K;
+  // compute-bound kernel addresses all of K from one base, the stream kernel at most
+  // 10 K-blocks, the rolling kernel uses 64-bit addresses), and its k-rows start
+  // 16-byte aligned (N % 16 == 0 always; M % 16 for A stored [K][M])
+  const char* name = kTable[id].name;
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t kreach = strncmp(name, "pipe", 4) == 0 ? K
+                         : strncmp(name, "stream", 6) == 0 ? 10 * kKBlock : 0;
   if (layout_in_place(id) && (!a_t || (kreach * M < lim && M % 16 == 0)) &&
       (!b_n || kreach * N < lim)) {
     maybe_print(kDense, M, N, K, 1, id);

@@ -95,26 +95,6 @@ struct StreamSrc {
   uint32_t a_step, b_step, b_hi;
 };
 
-// MN-contiguous staging: byte offset of chunk c of k-row kr, and a lane's offset for
-// the transposing reads of the 16 rows 16c..16c+15 of the tile: lane (g, p) receives
-// row 16c + p at k in [16g, 16g + 16) and [64 + 16g, 80 + 16g), the k order of the
-// K-contiguous operands. In one read the 32 k-rows 16g + 8h + j (g = 0..3, j = 0..7)
-// fall on every 16-byte bank group exactly twice, since k mod 4 and the swizzle
-// (k >> 4) & 3 = g both vary.
-__device__ __forceinline__ uint32_t mn_lds_off(int kr, int c) {
-  return (uint32_t)(kr * 64 + ((c ^ ((kr >> 4) & 3)) << 4));
-}
-__device__ __forceinline__ uint32_t mn_read_off(int lane, int c) {
-  const int g = lane >> 4, p = lane & 15;
-  return (uint32_t)((16 * g + (p >> 1)) * 64 + ((c ^ g) << 4) + 8 * (p & 1));
-}
-__device__ __forceinline__ v8i mn_frag(const uint8_t* tile, uint32_t off) {
-  const uint8_t* q = tile + off;
-  const v2i a = tr8_at(q), b = tr8_at(q + 8 * 64), c = tr8_at(q + 64 * 64),
-            d = tr8_at(q + 72 * 64);
-  return v8i{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
-
 // A lane's LDS offsets for the MN-contiguous paths: where its two B pieces go
 // (bw0, bw1), and its transposing-read offsets for B (b_rd) and the four A row groups.
 struct StreamLane {

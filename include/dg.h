@@ -119,11 +119,12 @@ dg_status dg_fp8_gemm_nt_noalloc(const void* A, const void* B, void* C, const fl
  * layout: sfA fp32 [M][K/128] (row m, K-block kb), sfB fp32 [ceil(N/128)][K/128]; C is
  * bf16 [M][N]. Same shape, alignment and error rules as dg_fp8_gemm_nt; the results
  * equal dg_fp8_gemm_nt's on the transposed operands bit for bit. The operands are
- * read in place (M % 16 == 0 is then required when A is stored [K][M]):
- *   - for M > 64, with K*M, K*N < 2^31 (nothing is allocated, as for the NT call);
- *   - for M <= 64 on the split-K stream kernel (K >= 2048 with at most 10 K-blocks per
- *     split, e.g. 64x2112x7168; DG_PRINT_CONFIGS names the kernel), with 1280*N < 2^31;
- *   - for M <= 64 with B stored [K][N] and K <= 1024 (the M > 64 kernel, in place).
+ * read in place, on the kernel the NT call of the same shape uses, when A stored
+ * [K][M] has M % 16 == 0 and
+ *   - M > 64: K*M, K*N < 2^31 (nothing is allocated, as for the NT call);
+ *   - M <= 64: 1280*N < 2^31 when the split-K stream kernel serves the shape (K >= 2048
+ *     with at most 10 K-blocks per split, e.g. 64x2112x7168; DG_PRINT_CONFIGS names
+ *     the kernel), no further condition on the rolling kernel (e.g. 64x32768x512).
  * Otherwise an operand that is not K-contiguous is first transposed into a
  * library-owned buffer of the stream (M*K or N*K bytes, kept and reused by later calls
  * on that stream, released by dg_release_workspaces() or at the end of the process).

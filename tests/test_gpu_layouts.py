@@ -5,12 +5,12 @@ must equal dg_fp8_gemm_nt on transposed copies of its operands bit for bit, up t
 full prefill shape.
 
 Two paths serve these calls. Shapes of the compute-bound kernel (M > 64) and of the
-M <= 64 stream kernel read the [K][M] / [K][N] operands in place (k-row tiles,
-transposing LDS reads): covered on both compute-bound tile shapes and both stream
-configurations, M and N tails, the dense tail split, split K, long K, and by capture
-into a HIP graph on a fresh stream, which succeeds only because nothing is allocated.
-A stored [K][M] with M % 16 != 0, and the M <= 64 shapes of the rolling kernel, go
-through a transposed copy: odd M, M = 1 and short K cover that path."""
+M <= 64 stream and rolling kernels read the [K][M] / [K][N] operands in place (k-row
+tiles, transposing LDS reads): covered on both compute-bound tile shapes, two stream
+and two rolling configurations, M and N tails, the dense tail split, split K, long K,
+and by capture into a HIP graph on a fresh stream, which succeeds only because nothing
+is allocated. A stored [K][M] with M % 16 != 0 goes through a transposed copy: odd M
+covers that path."""
 import numpy as np
 import pytest
 import torch
@@ -162,3 +162,24 @@ def test_decode_layout_gaussian(layout):
     g = run(layout, A, B, w.sfA, w.sfB, M, N)
     print(layout, assert_parity(g, oracle.gemm(A, B, w.sfA, w.sfB, layout), what=layout))
     assert np.array_equal(g, run("nt", w.A, w.B, w.sfA, w.sfB, M, N))
+
+
+SKINNY_MN = [(64, 32768, 512), (64, 2112, 1024), (16, 272, 384), (48, 80, 1280),
+             (37, 96, 640), (1, 16, 128), (32, 1072, 896), (64, 2560, 256)]
+
+
+@pytest.mark.parametrize("cfg", ["skinny_w4_tn1_d2", "skinny_w4_tn1_d8"])
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+def test_rolling_layouts_bitwise(cfg, layout, monkeypatch):
+    """M <= 64 on the rolling kernel: A stored [K][M] (M % 16 == 0) and B stored [K][N]
+    staged into each block's LDS slot and read transposed; the 64x32768x512 decode
+    shape, split K, column tails of 16 and 48, M = 1, 16, 32, 37, 48, 64 (37: A stored
+    [K][M] takes the copy path), column tiles grouped 4, 2 and 1 per XCD."""
+    monkeypatch.setenv("DG_FORCE_CONFIG", cfg)
+    for (M, N, K) in SKINNY_MN:
+        rng = np.random.default_rng(M + 7 * N + 5 * K + 3 * ord(layout[0]) + ord(layout[1]))
+        A_mk, B_nk, sfA, sfB = int_operands(rng, M, N, K)
+        A, B = stored(A_mk, B_nk, layout)
+        g = run(layout, A, B, sfA, sfB, M, N)
+        assert_bitwise(g, oracle.gemm(A, B, sfA, sfB, layout), what=f"{cfg} {layout} {M}x{N}x{K}")
+        assert np.array_equal(g, run("nt", A_mk, B_nk, sfA, sfB, M, N))
