@@ -568,15 +568,18 @@ bool print_configs() {
   return on;
 }
 
-void maybe_print(int kind, int64_t M, int64_t N, int64_t K, int32_t G, int id) {
+// One line per distinct (call, shape): the configuration, and for the NN / TN / TT calls
+// the operand layout and whether it is read in place or through a transposed copy.
+void maybe_print(int kind, int64_t M, int64_t N, int64_t K, int32_t G, int id,
+                 const char* note = "") {
   if (!print_configs()) return;
   static std::mutex mu;
-  static std::set<std::tuple<int, int64_t, int64_t, int64_t, int32_t>> seen;
+  static std::set<std::tuple<int, int64_t, int64_t, int64_t, int32_t, std::string>> seen;
   std::lock_guard<std::mutex> lock(mu);
-  if (!seen.insert(std::make_tuple(kind, M, N, K, G)).second) return;
+  if (!seen.insert(std::make_tuple(kind, M, N, K, G, std::string(note))).second) return;
   static const char* kinds[] = {"dense", "contiguous", "masked"};
-  fprintf(stderr, "[dg] %s M=%lld N=%lld K=%lld G=%d -> %s\n", kinds[kind], (long long)M,
-          (long long)N, (long long)K, G, kTable[id].name);
+  fprintf(stderr, "[dg] %s M=%lld N=%lld K=%lld G=%d -> %s%s\n", kinds[kind], (long long)M,
+          (long long)N, (long long)K, G, kTable[id].name, note);
 }
 
 dg_status launch(int kind, int id, const Problem& p, int64_t blocks, hipStream_t stream) {
@@ -931,7 +934,8 @@ dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
                          : strncmp(name, "stream", 6) == 0 ? 10 * kKBlock : 0;
   if (layout_in_place(id) && (!a_t || (kreach * M < lim && M % 16 == 0)) &&
       (!b_n || kreach * N < lim)) {
-    maybe_print(kDense, M, N, K, 1, id);
+    maybe_print(kDense, M, N, K, 1, id, a_t ? (b_n ? " (TN, in place)" : " (TT, in place)")
+                                             : " (NN, in place)");
     Problem p{};
     p.A = (const uint8_t*)A;
     p.B = (const uint8_t*)B;
@@ -947,6 +951,8 @@ dg_status gemm_layout(const void* A, const void* B, void* C, const float* sfA,
          : lay == kLayAT ? launch_layout<kLayAT>(id, p, st)
                          : launch_layout<kLayAT | kLayBN>(id, p, st);
   }
+  maybe_print(kDense, M, N, K, 1, id, a_t ? (b_n ? " (TN, transposed copy)" : " (TT, transposed copy)")
+                                           : " (NN, transposed copy)");
   uint8_t *a2 = nullptr, *b2 = nullptr;
   s = get_transpose_workspace(st, a_t ? (size_t)(M * K) : 0, b_n ? (size_t)(N * K) : 0, &a2, &b2);
   if (s != DG_OK) return s;

@@ -56,8 +56,10 @@
  *    thread-local message for the last failing call on the calling thread.
  *  - Zero-sized work (M, N or G*M_max == 0) returns DG_OK and launches nothing.
  *  - Environment: DG_PRINT_CONFIGS=1 prints the tile configuration chosen for each
- *    new (kind, shape) to stderr; DG_FORCE_CONFIG=<name> overrides the choice
- *    (tuning only, see dg_config_name).
+ *    new (kind, shape) to stderr, and for the NN / TN / TT calls whether the operands
+ *    are read in place or through a transposed copy (which uses a library-owned
+ *    buffer); DG_FORCE_CONFIG=<name> overrides the choice (tuning only, see
+ *    dg_config_name).
  */
 #ifndef DG_H_
 #define DG_H_

@@ -183,3 +183,36 @@ def test_rolling_layouts_bitwise(cfg, layout, monkeypatch):
         g = run(layout, A, B, sfA, sfB, M, N)
         assert_bitwise(g, oracle.gemm(A, B, sfA, sfB, layout), what=f"{cfg} {layout} {M}x{N}x{K}")
         assert np.array_equal(g, run("nt", A_mk, B_nk, sfA, sfB, M, N))
+
+
+def test_print_configs_names_the_layout_route(tmp_path):
+    """DG_PRINT_CONFIGS=1 (read once per process, so in a child process): an NN call on
+    the decode kernel reports "in place", a TN call with M % 16 != 0 "transposed copy"."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = tmp_path / "calls.py"
+    script.write_text(
+        "import sys\n"
+        f"sys.path.insert(0, {root!r})\n"
+        "import numpy as np, torch\n"
+        "from tests import gpu_util as gu\n"
+        "from tests.test_gpu_parity import int_operands\n"
+        "import fp8_block_scaled_dg_amd as dg\n"
+        "rng = np.random.default_rng(5)\n"
+        "for lay, (M, N, K) in (('nn', (64, 2112, 2048)), ('tn', (37, 96, 1536))):\n"
+        "    A, B, sfA, sfB = int_operands(rng, M, N, K)\n"
+        "    A = np.ascontiguousarray(A.T) if lay[0] == 't' else A\n"
+        "    B = np.ascontiguousarray(B.T) if lay[1] == 'n' else B\n"
+        "    c = torch.empty((M, N), dtype=torch.bfloat16, device='cuda')\n"
+        "    getattr(dg, 'fp8_gemm_' + lay)(gu.codes(A), gu.codes(B), c, gu.dev(sfA), gu.dev(sfB))\n"
+        "torch.cuda.synchronize()\n")
+    env = dict(os.environ, DG_PRINT_CONFIGS="1")
+    gu.announce("DG_PRINT_CONFIGS child process")
+    r = subprocess.run([sys.executable, str(script)], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [x for x in r.stderr.splitlines() if x.startswith("[dg] dense")]
+    assert any("M=64 N=2112 K=2048" in x and "(NN, in place)" in x for x in lines), lines
+    assert any("M=37 N=96 K=1536" in x and "(TN, transposed copy)" in x for x in lines), lines
