@@ -129,13 +129,21 @@ dg_status launch_pipe(const Problem& p0, int64_t blocks, hipStream_t stream) {
 
 using Pipe256x128 = PipeCfg<256, 128>;
 using Pipe128x256 = PipeCfg<128, 256>;
+using Pipe128x256L = PipeCfg<128, 256, 12>;  // long K: scales loaded per 12 K-blocks
+constexpr int kLongKB = 32;                  // K-blocks from which the 128x256 tiles use it
+
+// The 128x256-tile kernel, with the scale loads of its K length.
+template <int KIND, int LAY = 0>
+dg_status launch_pipe128(const Problem& p, int64_t blocks, hipStream_t stream) {
+  return p.K / kKBlock >= kLongKB ? launch_pipe<Pipe128x256L, KIND, LAY>(p, blocks, stream)
+                                  : launch_pipe<Pipe128x256, KIND, LAY>(p, blocks, stream);
+}
 
 // Grouped GEMM with the fused SwiGLU epilogue: p.N = 2 * I rows of B per expert
 // ([gate; up]); one 128x256 tile per 128 columns of h.
-template <int KIND>
-dg_status launch_pipe_swiglu(const Problem& p0, int64_t blocks, int64_t I, uint8_t* codes,
-                             float* sf, hipStream_t stream) {
-  using Cfg = Pipe128x256;
+template <class Cfg, int KIND>
+dg_status launch_pipe_swiglu_as(const Problem& p0, int64_t blocks, int64_t I, uint8_t* codes,
+                                float* sf, hipStream_t stream) {
   PipeArgs a{};
   a.p = p0;
   a.p.tiles_m = (int32_t)((p0.M + Cfg::BM - 1) / Cfg::BM);
@@ -155,6 +163,14 @@ dg_status launch_pipe_swiglu(const Problem& p0, int64_t blocks, int64_t I, uint8
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(DG_ERR_LAUNCH, "launch: %s", hipGetErrorString(err));
   return DG_OK;
+}
+
+template <int KIND>
+dg_status launch_pipe_swiglu(const Problem& p, int64_t blocks, int64_t I, uint8_t* codes,
+                             float* sf, hipStream_t stream) {
+  return p.K / kKBlock >= kLongKB
+             ? launch_pipe_swiglu_as<Pipe128x256L, KIND>(p, blocks, I, codes, sf, stream)
+             : launch_pipe_swiglu_as<Pipe128x256, KIND>(p, blocks, I, codes, sf, stream);
 }
 
 // ---------------------------------------------------------------- split-K workspace
@@ -481,8 +497,8 @@ const CfgEntry kTable[] = {
      launch_tile<Cfg64, kMasked>, 0, 0},
     {"pipe256x128", launch_pipe<Pipe256x128, kDense>, launch_pipe<Pipe256x128, kContiguous>,
      launch_pipe<Pipe256x128, kMasked>, 0, kPipeMaxKB},
-    {"pipe128x256", launch_pipe<Pipe128x256, kDense>, launch_pipe<Pipe128x256, kContiguous>,
-     launch_pipe<Pipe128x256, kMasked>, 0, kPipeMaxKB},
+    {"pipe128x256", launch_pipe128<kDense>, launch_pipe128<kContiguous>,
+     launch_pipe128<kMasked>, 0, kPipeMaxKB},
     {"skinny_w4_tn1_d3", launch_skinny<SkinnyCfg<4, 1, 3>>, nullptr, nullptr, 64, 0},
     {"skinny_w4_tn1_d2", launch_skinny<SkinnyCfg<4, 1, 2>>, nullptr, nullptr, 64, 0},
     {"skinny_w4_tn1_d5", launch_skinny<SkinnyCfg<4, 1, 5>>, nullptr, nullptr, 64, 0},
@@ -900,7 +916,7 @@ dg_status launch_layout(int id, const Problem& p, hipStream_t st) {
   if (strcmp(name, "skinny_w4_tn1_d5") == 0) return launch_skinny<SkinnyCfg<4, 1, 5>, LAY>(p, 1, st);
   if (strcmp(name, "skinny_w4_tn1_d8") == 0) return launch_skinny<SkinnyCfg<4, 1, 8>, LAY>(p, 1, st);
   if (strcmp(name, "pipe256x128") == 0) return launch_pipe<Pipe256x128, kDense, LAY>(p, 1, st);
-  return launch_pipe<Pipe128x256, kDense, LAY>(p, 1, st);
+  return launch_pipe128<kDense, LAY>(p, 1, st);
 }
 
 // The configuration reads MN-contiguous operands in place: the compute-bound kernels

@@ -44,9 +44,10 @@ namespace dg {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_>
+// SB_: K-blocks whose scales one scale load brings in (3, or 12 for 128-row tiles).
+template <int BM_, int BN_, int SB_ = 3>
 struct PipeCfg {
-  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int BM = BM_, BN = BN_, SB = SB_;
   static constexpr int WAVES_M = BM / 64, WAVES_N = BN / 64;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
@@ -62,6 +63,7 @@ struct PipeCfg {
   static_assert(NW == 8, "two waves per SIMD");
   static_assert(BN % 128 == 0, "tile columns nest in 128-column scale blocks");
   static_assert(A_DMA >= 1 && B_DMA >= 1 && RPW <= 32 && 32 % RPW == 0, "DMA split");
+  static_assert(SB == 3 || (SB == 12 && BM == 128), "scale batch");
 };
 
 constexpr int kPipeStageBytes = 49152;  // (256 + 128) * 128
@@ -71,10 +73,19 @@ static_assert(PipeCfg<128, 256>::STAGE == kPipeStageBytes, "stage size");
 __shared__ __align__(16) uint8_t pipe_stage0[kPipeStageBytes];
 __shared__ __align__(16) uint8_t pipe_stage1[kPipeStageBytes];
 __shared__ __align__(16) uint8_t pipe_stage2[kPipeStageBytes];
-// Scales of three consecutive K-blocks. Lane l of wave w's 12-byte sfA DMA puts
-// row (w * RPW + l % RPW)'s three values at byte w * 1024 + 16 * l of pipe_scale.
-// Every wave's sfB DMA writes the same bytes to pipe_sfb: lane l holds the tile's
-// sfB row nb0 + min(l, BN/128 - 1) at byte 16 * l (identical concurrent writes).
+// Scales. Cfg::SB = 3: those of three consecutive K-blocks; lane l of wave w's 12-byte
+// sfA DMA puts row (w * RPW + l % RPW)'s three values at byte w * 1024 + 16 * l of
+// pipe_scale, and every wave's sfB DMA writes the same bytes to pipe_sfb: lane l holds
+// the tile's sfB row nb0 + min(l, BN/128 - 1) at byte 16 * l (identical concurrent
+// writes).
+// Cfg::SB = 12 (128-row tiles, long K): those of twelve consecutive K-blocks, loaded
+// once per twelve blocks: every row's 48 bytes (fp32) or 16 bytes (the packed UE8M0
+// words that hold the twelve bytes) sit at pipe_scale + row * 48 (or 16), as 16-byte
+// chunks in lane order over the eight waves' DMAs, and the tile's sfB rows likewise at
+// pipe_sfb + row * 48. Each load touches every row of the tile once, so twelve blocks
+// per load instead of three cut the cache lines the scale loads touch fourfold
+// (prefill 514 -> 506 us, contiguous 368 -> 360 us). With few K-blocks per tile the
+// longer set-up it needs costs more than it saves (masked, 16 K-blocks: 142 -> 147 us).
 constexpr int kScaleWaveBytes = 1024;
 __shared__ __align__(16) uint8_t pipe_scale[8 * kScaleWaveBytes];
 __shared__ __align__(16) uint8_t pipe_sfb[1024];
@@ -125,10 +136,11 @@ struct PipeThread {
   uint32_t a_kstep, b_kstep;
   uint32_t a_off[Cfg::A_DMA];
   uint32_t b_off[Cfg::B_DMA];
-  uint32_t sa_off;  // this lane's sfA row
-  uint32_t sb_off;  // this lane's sfB row
+  uint32_t sa_off;  // this lane's sfA row (and, 128-row tiles, chunk)
+  uint32_t sb_off;  // this lane's sfB row (and chunk)
   int sa_shift;     // sfA's scalar offset for K-block kb is (kb >> sa_shift) * 4 bytes:
                     // 0 for fp32 values, 2 for packed UE8M0 words (nonzero = packed)
+  int kb_lo;        // first K-block of the run: scale batches start at kb_lo + 12 j
 };
 
 // Raw buffer over [p, p + bytes), bytes < 2^31.
@@ -139,6 +151,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p,
                                            0x00020000);
 }
 
+// The scale DMAs issued with K-block kb's operand DMAs when kb starts a group of three
+// blocks (relative to the run's first block): with Cfg::SB = 3 the three blocks'
+// scales; with Cfg::SB = 12 twelve blocks' scales when kb also starts a group of
+// twelve, and nothing otherwise. Scales are read only at the start of a group of three,
+// before the barrier after which this refill is issued, so one buffer serves.
+template <class Cfg>
+__device__ __forceinline__ void pipe_issue_scales(const PipeThread<Cfg>& th, int kb, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (Cfg::SB == 12) {
+    if ((kb - th.kb_lo) % Cfg::SB == 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sa_rsrc,
+                                               DG_LDS(pipe_scale + wave * kScaleWaveBytes), 16,
+                                               th.sa_off, (kb >> th.sa_shift) << 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sb_rsrc, DG_LDS(pipe_sfb), 16, th.sb_off,
+                                               kb * 4, 0, 0);
+    }
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sa_rsrc,
+                                             DG_LDS(pipe_scale + wave * kScaleWaveBytes), 12,
+                                             th.sa_off, (kb >> th.sa_shift) << 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sb_rsrc, DG_LDS(pipe_sfb), 12, th.sb_off, kb * 4,
+                                             0, 0);
+  }
+#endif
+}
+
 // The DMAs of K-block kb into stage S. With SCALES (kb a multiple of 3) the batch
 // starts with the scales of K-blocks kb..kb+2 (the wave's share of sfA rows and its
 // copy of the tile's sfB rows) into pipe_scale. They go first, so that a wait that
@@ -146,13 +184,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p,
 template <class Cfg, int S, bool SCALES>
 __device__ __forceinline__ void pipe_issue(const PipeThread<Cfg>& th, int kb, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
-  if (SCALES) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sa_rsrc,
-                                             DG_LDS(pipe_scale + wave * kScaleWaveBytes), 12,
-                                             th.sa_off, (kb >> th.sa_shift) << 2, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sb_rsrc, DG_LDS(pipe_sfb), 12, th.sb_off, kb * 4,
-                                             0, 0);
-  }
+  if (SCALES) pipe_issue_scales<Cfg>(th, kb, wave);
   uint8_t* st = pipe_stage<S>();
   const int koff_a = kb * th.a_kstep, koff_b = kb * th.b_kstep;
 #pragma unroll
@@ -173,13 +205,7 @@ __device__ __forceinline__ void pipe_issue(const PipeThread<Cfg>& th, int kb, in
 template <class Cfg, int S, bool SCALES, int LO, int HI>
 __device__ __forceinline__ void pipe_issue_ops(const PipeThread<Cfg>& th, int kb, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  if (SCALES && LO == 0) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sa_rsrc,
-                                             DG_LDS(pipe_scale + wave * kScaleWaveBytes), 12,
-                                             th.sa_off, (kb >> th.sa_shift) << 2, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(th.sb_rsrc, DG_LDS(pipe_sfb), 12, th.sb_off, kb * 4,
-                                             0, 0);
-  }
+  if (SCALES && LO == 0) pipe_issue_scales<Cfg>(th, kb, wave);
   uint8_t* st = pipe_stage<S>();
   const int koff_a = kb * th.a_kstep, koff_b = kb * th.b_kstep;
 #pragma unroll
@@ -264,7 +290,7 @@ struct PipeLane {
     const int c = (r0 + 32 * t + 16 * (q & 1)) >> 4;
     return (uint32_t)(krow * ROW + ((c ^ tswz(krow, ROW / 16)) << 4) + 8 * half);
   }
-  __device__ __forceinline__ PipeLane(int wave, int lane) {
+  __device__ __forceinline__ PipeLane(int wave, int lane, bool packed) {
     const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
     const int r32 = lane & 31, g = lane >> 5;
     const int sw = swz(r32);
@@ -284,9 +310,16 @@ struct PipeLane {
       vb[1] = (uint32_t)Cfg::OFF_B + toff<Cfg::BN>(lane, wn * 64, 1);
     }
     const int ra0 = wm * 64 + r32, ra1 = ra0 + 32;
-    sa0 = (uint32_t)((ra0 / Cfg::RPW) * kScaleWaveBytes + (ra0 % Cfg::RPW) * 16);
-    sa1 = (uint32_t)((ra1 / Cfg::RPW) * kScaleWaveBytes + (ra1 % Cfg::RPW) * 16);
-    sb = (uint32_t)(((wn * 64) / 128) * 16);
+    if (Cfg::SB == 12) {
+      const int row_bytes = packed ? 16 : 4 * Cfg::SB;
+      sa0 = (uint32_t)(ra0 * row_bytes);
+      sa1 = (uint32_t)(ra1 * row_bytes);
+      sb = (uint32_t)(((wn * 64) / 128) * 4 * Cfg::SB);
+    } else {
+      sa0 = (uint32_t)((ra0 / Cfg::RPW) * kScaleWaveBytes + (ra0 % Cfg::RPW) * 16);
+      sa1 = (uint32_t)((ra1 / Cfg::RPW) * kScaleWaveBytes + (ra1 % Cfg::RPW) * 16);
+      sb = (uint32_t)(((wn * 64) / 128) * 16);
+    }
   }
 };
 
@@ -376,7 +409,33 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
 
   v8i a10, a11;
   if (HI) read_a(st, pl, 1, a10, a11);
-  if (S == 0) {
+  if (S == 0 && Cfg::SB == 12) {
+    // scales of K-blocks kb..kb+2 (landed before the previous barrier), at position
+    // r = (kb - kb_lo) % 12 of the twelve-block group starting at b0 = kb - r: three fp32
+    // values from float r of the row, or (packed) bytes (b0 % 4) + r .. of the words
+    // from b0 / 4 on
+    const int r = (kb - th.kb_lo) % Cfg::SB;
+    const float* bsf = (const float*)(pipe_sfb + pl.sb) + r;
+    float a0[3], a1[3];
+    if (th.sa_shift) {
+      const int o = ((kb - r) & 3) + r;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        a0[j] = ue8m0_value(pipe_scale[pl.sa0 + o + j]);
+        a1[j] = ue8m0_value(pipe_scale[pl.sa1 + o + j]);
+      }
+    } else {
+      const float* x0 = (const float*)(pipe_scale + pl.sa0) + r;
+      const float* x1 = (const float*)(pipe_scale + pl.sa1) + r;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) a0[j] = x0[j], a1[j] = x1[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      sc.s0[j] = a0[j] * bsf[j];
+      sc.s1[j] = a1[j] * bsf[j];
+    }
+  } else if (S == 0) {
     // scales of K-blocks kb..kb+2 (landed before the previous barrier): three fp32
     // values, or (packed) bytes kb % 4 .. kb % 4 + 2 of the words from kb / 4 on
     const v4f b = *(const v4f*)(pipe_sfb + pl.sb);
@@ -543,13 +602,36 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
         th.b_off[q] = (uint32_t)Rg * (uint32_t)K + (uint32_t)((c ^ swz(R)) << 4);
       }
     }
-    int arow = wave * Cfg::RPW + (lane % Cfg::RPW);
-    if (arow >= a_rows) arow = a_rows - 1;
-    th.sa_off = (uint32_t)arow * (uint32_t)rb;
-    int nb = lane < Cfg::BN / 128 ? lane : Cfg::BN / 128 - 1;
-    if (nb >= 1) nb += b_hi / 128;
-    if (nb0 + nb >= NB) nb = NB - 1 - nb0;
-    th.sb_off = (uint32_t)nb * (uint32_t)KB * 4u;
+    th.kb_lo = kb_lo;
+    if (Cfg::SB == 12) {
+      // 16-byte chunk i = 64 wave + lane of the tile's twelve-block scale group: row
+      // i / 3, chunk i % 3 (fp32), or row i (packed); lanes past the last chunk repeat
+      // it (their LDS bytes are never read)
+      int i = wave * 64 + lane, arow = i, chunk = 0;
+      if (p.sfa_packed) {
+        arow = i < 128 ? i : 127;
+      } else {
+        if (i >= 384) i = 383;
+        arow = i / 3;
+        chunk = i - 3 * arow;
+      }
+      if (arow >= a_rows) arow = a_rows - 1;
+      th.sa_off = (uint32_t)arow * (uint32_t)rb + (uint32_t)(chunk * 16);
+      // sfB: the tile's BN / 128 rows, three chunks each, in lanes 0 .. 3 BN / 128 - 1
+      int l = lane < 3 * (Cfg::BN / 128) ? lane : 3 * (Cfg::BN / 128) - 1;
+      int nb = l / 3;
+      if (nb >= 1) nb += b_hi / 128;
+      if (nb0 + nb >= NB) nb = NB - 1 - nb0;
+      th.sb_off = (uint32_t)nb * (uint32_t)KB * 4u + (uint32_t)((l % 3) * 16);
+    } else {
+      int arow = wave * Cfg::RPW + (lane % Cfg::RPW);
+      if (arow >= a_rows) arow = a_rows - 1;
+      th.sa_off = (uint32_t)arow * (uint32_t)rb;
+      int nb = lane < Cfg::BN / 128 ? lane : Cfg::BN / 128 - 1;
+      if (nb >= 1) nb += b_hi / 128;
+      if (nb0 + nb >= NB) nb = NB - 1 - nb0;
+      th.sb_off = (uint32_t)nb * (uint32_t)KB * 4u;
+    }
   }
 
 #pragma unroll
@@ -558,7 +640,7 @@ __device__ __forceinline__ void pipe_mainloop_as(const Problem& p, const TileVie
     for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
   v16f carry[2] = {v16f{}, v16f{}};
   float carry_s = 0.f;
-  const PipeLane<Cfg, LAY> pl(wave, lane);
+  const PipeLane<Cfg, LAY> pl(wave, lane, p.sfa_packed != 0);
   Frag0 f;
   PipeScales sc;
 
