@@ -241,6 +241,10 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* p, uint32_t lo, uint32_t h
 }
 
 #define DG_FENCE() __builtin_amdgcn_sched_barrier(0)
+// An empty volatile asm that reads and rewrites x: the instructions producing x cannot
+// move past it. The scheduling fences above bind the machine scheduler only; code
+// motion before it (sinking arithmetic into a later basic block) ignores them.
+#define DG_PIN(x) asm volatile("" : "+v"(x))
 
 __device__ __forceinline__ v16f mfma32(const v8i& b, const v8i& a, const v16f& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
@@ -387,7 +391,10 @@ struct PipeScales {
 // block kb is done, so the DMA of block kb+3 refills kb's stage, and A tile 0 and
 // B tile 1 of kb+1 are read (B tile 1 into spare registers). B tile 0 of kb+1 is
 // read after M7, when kb's is dead. Scheduling fences keep this order; the compiler
-// inserts only the LDS waits.
+// inserts only the LDS waits. The carried promotions are pinned before the barrier:
+// in the step that may issue the scale DMAs (a branch after M5) the compiler otherwise
+// sinks them past that branch, behind the barrier, and prefill and the contiguous
+// layout measured 1-3 % slower that way.
 template <class Cfg, int S, int MODE, int LAY>
 __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeLane<Cfg, LAY>& pl,
                                           v16f (&acc)[2][2], Frag0& f, v16f (&carry)[2],
@@ -464,16 +471,16 @@ __device__ __forceinline__ void pipe_step(const PipeThread<Cfg>& th, const PipeL
   }
   DG_FENCE();
   v16f p00 = mfma32(f.b0, f.a0, zero);  // M1
-  if (HI) promote8<0>(acc[1][0], carry[0], carry_s);
+  if (HI) { promote8<0>(acc[1][0], carry[0], carry_s); DG_PIN(acc[1][0]); }
   DG_FENCE();
   v16f p01 = mfma32(f.c0, f.a0, zero);  // M2
-  if (HI) promote8<8>(acc[1][0], carry[0], carry_s);
+  if (HI) { promote8<8>(acc[1][0], carry[0], carry_s); DG_PIN(acc[1][0]); }
   DG_FENCE();
   p00 = mfma32(f.b1, f.a1, p00);  // M3
-  if (HI) promote8<0>(acc[1][1], carry[1], carry_s);
+  if (HI) { promote8<0>(acc[1][1], carry[1], carry_s); DG_PIN(acc[1][1]); }
   DG_FENCE();
   p01 = mfma32(f.c1, f.a1, p01);  // M4
-  if (HI) promote8<8>(acc[1][1], carry[1], carry_s);
+  if (HI) { promote8<8>(acc[1][1], carry[1], carry_s); DG_PIN(acc[1][1]); }
   DG_FENCE();
   // block kb+1 in LDS, block kb's stage free. Block kb+3's DMAs into it are spread
   // over M5..M8, a quarter behind each (instead of all eight waves queueing a whole
