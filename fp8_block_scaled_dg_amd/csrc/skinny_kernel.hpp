@@ -22,9 +22,11 @@
 // share, so lane (g, r) of a fragment holds k in [16g, 16g+16) and [64+16g, 80+16g)
 // for both operands. Each B load instruction then reads 64 contiguous bytes of every
 // row it touches (whole cache-line halves) rather than four scattered 16-byte pieces.
-// Every load is unconditional, its block index clamped into the unit's range (the
-// pipeline's tail re-reads the last block, a cache hit), so the compiler's waits are
-// exact: computing block t waits for block t only.
+// Every load inside the loop is unconditional, its block index clamped into the unit's
+// range, so the compiler's waits are exact: computing block t waits for block t only.
+// The unit's last D blocks are computed after the loop with nothing more issued (a
+// tail that re-read the last block instead was 13 % slower on 64x32768x512, whose
+// units are 4 blocks: half again as many loads).
 //
 // Operands stored MN-contiguous (LAY bits; 64-column workgroups, W = 4, TN = 1), the
 // NN / TN / TT layouts of the DeepGEMM project page (aiproducthub.cn, "core
@@ -265,26 +267,37 @@ __global__ void __launch_bounds__(Cfg::NT) skinny_kernel(SkinnyArgs args) {
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // ---- the pipeline: block t lives in stage/slot t % D (static within the body)
-  for (int t0 = 0; t0 < ks; t0 += D) {
+  auto stage_in = [&](int j) {
+    uint8_t* slot = lds + j * SLOT;
+#pragma unroll
+    for (int u = 0; u < A_PER; ++u) *(v4u*)(slot + src.a_dst[u]) = st[j].a[u];
+    if (wave == 0) ((float*)(slot + 64 * kKBlock))[lane] = st[j].sa;
+    if constexpr ((LAY & kLayBN) != 0) {
+      const v8i& v = st[j].b[0];
+      *(v4u*)(slot + Cfg::SLOT + L.bw0) =
+          v4u{(unsigned)v[0], (unsigned)v[1], (unsigned)v[2], (unsigned)v[3]};
+      *(v4u*)(slot + Cfg::SLOT + L.bw1) =
+          v4u{(unsigned)v[4], (unsigned)v[5], (unsigned)v[6], (unsigned)v[7]};
+    }
+    __syncthreads();  // block t's A tile and sfA column (and B tile) are in the slot
+  };
+  int t0 = 0;
+  for (; t0 + D < ks; t0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int t = t0 + j;
-      uint8_t* slot = lds + j * SLOT;
-#pragma unroll
-      for (int u = 0; u < A_PER; ++u) *(v4u*)(slot + src.a_dst[u]) = st[j].a[u];
-      if (wave == 0) ((float*)(slot + 64 * kKBlock))[lane] = st[j].sa;
-      if constexpr ((LAY & kLayBN) != 0) {
-        const v8i& v = st[j].b[0];
-        *(v4u*)(slot + Cfg::SLOT + L.bw0) =
-            v4u{(unsigned)v[0], (unsigned)v[1], (unsigned)v[2], (unsigned)v[3]};
-        *(v4u*)(slot + Cfg::SLOT + L.bw1) =
-            v4u{(unsigned)v[4], (unsigned)v[5], (unsigned)v[6], (unsigned)v[7]};
-      }
-      __syncthreads();  // block t's A tile and sfA column (and B tile) are in the slot
-      if (t < ks) skinny_mma<Cfg, LAY>(acc, slot, st[j].b, sfb[t], g, l16, L);
+      stage_in(j);
+      skinny_mma<Cfg, LAY>(acc, lds + j * SLOT, st[j].b, sfb[t], g, l16, L);
       const int tn = t + D;
       skinny_issue<Cfg, PACKED>(st[j], src, tn < ks ? tn : ks - 1);
     }
+  }
+  // the last D blocks (or fewer): nothing more to issue
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const int t = t0 + j;
+    stage_in(j);
+    if (t < ks) skinny_mma<Cfg, LAY>(acc, lds + j * SLOT, st[j].b, sfb[t], g, l16, L);
   }
 
   // ---- split reduction (S > 1): partial out, last arriving split sums in order.
