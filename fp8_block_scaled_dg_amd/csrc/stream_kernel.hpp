@@ -9,9 +9,9 @@
 //      and each wave's B fragments straight into MFMA operand registers; before
 //      them the sfA column block (LDS DMA) and the wave's sfB values (registers).
 //   2. For block t = 0..D-1 in order: wait until this wave's loads up to block t
-//      have landed (vmcnt counts the later blocks' loads, all compile-time; with B
-//      stored [N][K] one wait and barrier covers a group of three blocks), one
-//      barrier so that every wave's DMA share of the A tile is visible, then per
+//      have landed (vmcnt counts the later blocks' loads, all compile-time; one wait
+//      and barrier covers a group of three blocks), one barrier so that every
+//      wave's DMA share of the A tile is visible, then per
 //      16x16 tile one v_mfma_f32_16x16x128_f8f6f4 gives the block partial and it is
 //      promoted into the fp32 accumulators with sfA[m][kb] * sfB[n/128][kb] -- the
 //      two-level accumulation of the DeepGEMM launch article (deepseek.csdn.net),
@@ -37,9 +37,10 @@
 //   - A stored [K][M]: the block's A tile arrives by LDS DMA in that layout;
 //   - B stored [K][N]: each lane still loads two 16-byte k-row pieces per block into
 //     registers (so every load of the unit is in flight at once, as for B stored
-//     [N][K]). During block t the wave writes block t+1's pieces into a three-block
-//     LDS ring, so the writes overlap block t's work; the barrier of block t+1 makes
-//     them visible, and the transposing reads follow it.
+//     [N][K]). At the first block of each group of three, after the group's loads
+//     have landed, the wave writes the group's pieces into one of two sets of three
+//     LDS slots; the group's barrier makes them visible, and the transposing reads
+//     follow it.
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -66,7 +67,7 @@ template <int I>
 __shared__ __align__(16) uint8_t stream_a[64 * kKBlock];  // A tile of block I
 __shared__ __align__(16) uint8_t stream_sfa[3 * 1024];     // sfA: [group][row][4]
 __shared__ __align__(16) uint16_t stream_out[64 * 128];    // bf16 output staging
-__shared__ __align__(16) uint8_t stream_bt[3][128 * 64];   // B stored [K][N]: 3-block ring
+__shared__ __align__(16) uint8_t stream_bt[6][128 * 64];   // B stored [K][N]: two 3-block sets
 
 struct StreamArgs {
   Problem p;
@@ -145,10 +146,11 @@ __device__ __forceinline__ void stream_issue_all(StreamRegs<Cfg>& r, const Strea
   }
 }
 
-// K-blocks per wait and barrier with B stored [N][K]. The blocks' data arrives in issue
-// order over the whole stream, so the waves still compute a group as soon as its last
-// block has landed; on 64x2112x7168 groups of 3 or 5 measured 2.4 % faster than a
-// barrier per block (11.60 against 11.89 us), and one wait for all ten blocks 3 % slower.
+// K-blocks per wait and barrier. The blocks' data arrives in issue order over the whole
+// stream, so the waves still compute a group as soon as its last block has landed; on
+// 64x2112x7168 groups of 3 or 5 measured 2.4 % faster than a barrier per block (11.60
+// against 11.89 us), one wait for all ten blocks 3 % slower; with B stored [K][N] the
+// grouped ring measured 3.6 % faster than a per-block one.
 constexpr int kSyncBlocks = 3;
 
 template <class Cfg, int T, bool PACKED, int LAY>
@@ -156,25 +158,25 @@ __device__ __forceinline__ void stream_compute(v4f (&acc)[Cfg::TM][Cfg::TN], con
                                                const StreamLane& L, int ks, int g, int l16,
                                                int shift) {
   if constexpr (T < Cfg::D) {
-    // B stored [N][K]: at the first block of each group of kSyncBlocks, this wave's
-    // loads of every block of the group have landed, and every wave's A DMAs of those
-    // blocks are visible after the barrier; the group's other blocks need neither.
-    // B stored [K][N]: this wave's loads of blocks 0..T have landed; every wave's A DMAs
-    // of block T are visible after the barrier. Block T's pieces were written into ring
-    // slot T % 3 during block T - 1 (block 0's here), and this wave's wait above
-    // (lgkmcnt 0) completed its writes before the barrier. Block T + 1's pieces go to
-    // slot (T + 1) % 3, last read in block T - 2: every wave finished those reads before
-    // it reached the barrier of block T - 1, which this wave has passed.
+    // At the first block of each group of kSyncBlocks, this wave's loads of every block
+    // of the group have landed, and every wave's A DMAs of those blocks are visible after
+    // the barrier; the group's other blocks need neither. B stored [K][N]: before that
+    // barrier each wave writes its pieces of the group's blocks into the group's set of
+    // ring slots (sets alternate between groups) and waits for the writes (lgkmcnt 0).
+    // A set is rewritten two groups later: every wave finished reading it before it
+    // reached the barrier of the group in between, which this wave has passed.
     constexpr bool RING = (LAY & kLayBN) != 0;
-    constexpr bool SYNC = RING || T % kSyncBlocks == 0;
-    constexpr int LAST = RING ? T : (T + kSyncBlocks - 1 < Cfg::D ? T + kSyncBlocks - 1 : Cfg::D - 1);
+    constexpr int G = kSyncBlocks;
+    constexpr bool SYNC = T % G == 0;
+    constexpr int LAST = T + G - 1 < Cfg::D ? T + G - 1 : Cfg::D - 1;
+    constexpr int SET = ((T / G) % 2) * G;  // first ring slot of this group
     if constexpr (SYNC) stream_wait<(Cfg::D - 1 - LAST) * Cfg::OPB>();
-    if constexpr (RING) {
-      if (T == 0) {
-        stream_ring_write(stream_bt[0], L, r.b[0][0]);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0, vmcnt and expcnt untouched
-      }
-      if (T + 1 < Cfg::D && T + 1 < ks) stream_ring_write(stream_bt[(T + 1) % 3], L, r.b[T + 1][0]);
+    if constexpr (RING && SYNC) {
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (T + j <= LAST && T + j < ks)
+          stream_ring_write(stream_bt[SET + j], L, r.b[T + j < Cfg::D ? T + j : 0][0]);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0, vmcnt and expcnt untouched
     }
     if constexpr (SYNC) __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -201,7 +203,7 @@ __device__ __forceinline__ void stream_compute(v4f (&acc)[Cfg::TM][Cfg::TN], con
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         if constexpr ((LAY & kLayBN) != 0)
-          bf[j] = mn_frag(stream_bt[T % 3], L.b_rd);
+          bf[j] = mn_frag(stream_bt[SET + T % G], L.b_rd);
         else
           bf[j] = r.b[T][j];
       }
