@@ -165,7 +165,8 @@ def test_decode_layout_gaussian(layout):
 
 
 SKINNY_MN = [(64, 32768, 512), (64, 2112, 1024), (16, 272, 384), (48, 80, 1280),
-             (37, 96, 640), (1, 16, 128), (32, 1072, 896), (64, 2560, 256)]
+             (37, 96, 640), (1, 16, 128), (32, 1072, 896), (64, 2560, 256),
+             (64, 8192, 640)]  # K runs of 3 and 2 blocks
 
 
 @pytest.mark.parametrize("cfg", ["skinny_w4_tn1_d2", "skinny_w4_tn1_d8"])

@@ -425,7 +425,10 @@ def all_configs():
 @pytest.mark.parametrize("cfg", all_configs())
 def test_every_config_dense_integer_exact(cfg, force_config):
     force_config(cfg)
-    shapes = [(64, 2112, 1024), (37, 272, 384), (1, 16, 128), (64, 2112, 1664), (50, 1040, 7168)]
+    shapes = [(64, 2112, 1024), (37, 272, 384), (1, 16, 128), (64, 2112, 1664), (50, 1040, 7168),
+              # K runs of 3 and 2 blocks (64x8192x640: 128 column tiles, 2 splits) and of
+              # 3 (48x16384x384: one split): the rolling kernel's loop and tail both run
+              (64, 8192, 640), (48, 16384, 384)]
     if not cfg.startswith("skinny"):
         shapes += [(300, 400, 512), (129, 144, 256)]
     for (M, N, K) in shapes:
