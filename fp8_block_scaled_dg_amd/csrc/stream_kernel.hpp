@@ -8,11 +8,11 @@
 //      A tile (64 x 128 bytes) by LDS DMA into that block's own __shared__ array,
 //      and each wave's B fragments straight into MFMA operand registers; before
 //      them the sfA column block (LDS DMA) and the wave's sfB values (registers).
-//   2. For block t = 0..D-1 in order: wait until this wave's loads up to block t
-//      have landed (vmcnt counts the later blocks' loads, all compile-time; one wait
-//      and barrier covers a group of three blocks), one barrier so that every
-//      wave's DMA share of the A tile is visible, then per
-//      16x16 tile one v_mfma_f32_16x16x128_f8f6f4 gives the block partial and it is
+//   2. For each group of three blocks in order: wait until this wave's loads up to
+//      the group's last block have landed (vmcnt counts the later blocks' loads, all
+//      compile-time), one barrier so that every wave's DMA share of the group's A
+//      tiles is visible, then for each block of the group and each 16x16 tile one
+//      v_mfma_f32_16x16x128_f8f6f4 gives the block partial and it is
 //      promoted into the fp32 accumulators with sfA[m][kb] * sfB[n/128][kb] -- the
 //      two-level accumulation of the DeepGEMM launch article (deepseek.csdn.net),
 //      section 1.2 "precision safeguards".
