@@ -465,7 +465,7 @@ def main():
                          "time has passed, so that the GPU clocks have left their idle state "
                          "(0: exactly --warmup steps, e.g. under a profiler)")
     ap.add_argument("--workload", default="decode",
-                    choices=sorted(WORKLOADS) + ["hbm_ceiling", "vendor_prefill"])
+                    choices=sorted(WORKLOADS) + ["hbm_ceiling", "vendor_prefill", "vendor_decode"])
     ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
                     help="graph: the K launches of each GEMM are captured into a HIP graph "
                          "and replayed (no host launch gaps); eager: launched from Python")
@@ -521,6 +521,9 @@ def main():
         return
     if args.workload == "vendor_prefill":
         print(json.dumps(vendor_prefill(args.steps, rotate)), flush=True)
+        return
+    if args.workload == "vendor_decode":
+        print(json.dumps(vendor_decode(args.steps, rotate)), flush=True)
         return
     names = WORKLOADS[args.workload]
     if args.gemm is not None:
@@ -688,52 +691,82 @@ def mfma_ceiling(iters: int = 2000, reps: int = 10):
     return flops / (ms * 1e-3) / 1e12, (mhz / 1e3 if mhz else None)
 
 
-def vendor_prefill(K: int, rotate: int) -> dict:
+def vendor_gemm(names, K: int, rotate: int, graph: bool) -> dict:
     """A reference point, not this library: the vendor FP8 GEMM (torch._scaled_mm, which
-    calls hipBLASLt) on the prefill shape 4096x7168x18432 with the same e4m3fn codes,
-    with one scale per tensor and with one scale per row of A and per column of B.
-    Neither form applies a scale per 128-wide K-block, so it computes a different
-    product and its output is not checked; it shows what a tuned FP8 GEMM without
-    per-block promotion reaches on this GPU. Eager launches (a launch gap is small
-    beside a kernel of hundreds of microseconds), inputs rotating like the prefill leg."""
+    calls hipBLASLt) on the named dense workloads with the same e4m3fn codes, with one
+    scale per tensor and with one scale per row of A and per column of B. Neither form
+    applies a scale per 128-wide K-block, so it computes a different product and its
+    output is not checked; it shows what a tuned FP8 GEMM without per-block promotion
+    reaches on this GPU. Inputs rotate like this library's legs; graph: the K launches
+    are replayed from a HIP graph (the decode shapes, whose kernels are shorter than a
+    host launch), else launched eagerly (prefill, where the launch gap is negligible)."""
     import torch
     import synth
-    w = synth.workload("prefill")
-    M, N, Kd = w.shape[:3]
     dev = "cuda:0"
     fp8 = torch.float8_e4m3fn
-    footprint = M * Kd + N * Kd + 2 * M * N
-    copies = max(1, min(MAX_COPIES, -(-rotate // footprint)))
-    A0 = torch.from_numpy(w.A).to(dev).view(fp8)
-    B0 = torch.from_numpy(w.B).to(dev).view(fp8)
-    sets = [dict(A=A0.clone(), B=B0.clone(), C=torch.empty(M, N, dtype=torch.bfloat16, device=dev))
-            for _ in range(copies)]
-    del A0, B0
-    forms = {"per_tensor": (torch.ones((), device=dev), torch.ones((), device=dev)),
-             "rowwise": (torch.ones(M, 1, device=dev), torch.ones(1, N, device=dev))}
     out = {}
-    for form, (sa, sb) in forms.items():
-        def launch(i, sa=sa, sb=sb):
-            st = sets[i % copies]
-            torch._scaled_mm(st["A"], st["B"].t(), sa, sb, out_dtype=torch.bfloat16, out=st["C"])
-        t0 = time.perf_counter()
-        i = 0
-        while time.perf_counter() - t0 < 0.5 or i < 20:
-            launch(i)
-            i += 1
-            if i % 20 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        ms = timed_launches(launch, K, i, False)
-        out[form] = dict(avg_us=ms * 1e3, tflops=2.0 * M * N * Kd / (ms * 1e-3) / 1e12)
-    best = max(out.values(), key=lambda d: d["tflops"])
+    for name in names:
+        w = synth.workload(name)
+        M, N, Kd = w.shape[:3]
+        footprint = M * Kd + N * Kd + 2 * M * N
+        copies = max(1, min(MAX_COPIES, -(-rotate // footprint)))
+        A0 = torch.from_numpy(w.A).to(dev).view(fp8)
+        B0 = torch.from_numpy(w.B).to(dev).view(fp8)
+        sets = [dict(A=A0.clone(), B=B0.clone(),
+                     C=torch.empty(M, N, dtype=torch.bfloat16, device=dev))
+                for _ in range(copies)]
+        del A0, B0
+        forms = {"per_tensor": (torch.ones((), device=dev), torch.ones((), device=dev)),
+                 "rowwise": (torch.ones(M, 1, device=dev), torch.ones(1, N, device=dev))}
+        res = {}
+        for form, (sa, sb) in forms.items():
+            def launch(i, sa=sa, sb=sb):
+                st = sets[i % copies]
+                torch._scaled_mm(st["A"], st["B"].t(), sa, sb, out_dtype=torch.bfloat16,
+                                 out=st["C"])
+            t0 = time.perf_counter()
+            i = 0
+            while time.perf_counter() - t0 < 0.5 or i < 20:
+                launch(i)
+                i += 1
+                if i % 20 == 0:
+                    torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            ms = timed_launches(launch, K, i, graph)
+            res[form] = dict(avg_us=ms * 1e3, tflops=2.0 * M * N * Kd / (ms * 1e-3) / 1e12,
+                             gbs=(M * Kd + N * Kd + 2 * M * N) / (ms * 1e-3) / 1e9)
+        out[name] = dict(shape=dict(M=M, N=N, K=Kd), rotation_copies=copies, forms=res)
+    return out
+
+
+def vendor_prefill(K: int, rotate: int) -> dict:
+    """The vendor reference on the prefill shape 4096x7168x18432 (see vendor_gemm)."""
+    r = vendor_gemm(["prefill"], K, rotate, False)["prefill"]
+    best = max(r["forms"].values(), key=lambda d: d["tflops"])
     return {"metric": "vendor FP8 GEMM TFLOPS on 4096x7168x18432 (reference point)",
             "value": best["tflops"], "unit": "TFLOPS", "n_gpus": 1, "steps": K,
             "higher_is_better": True, "dtype": "fp8", "data": "synthetic",
             "config": {"workload": "torch._scaled_mm (hipBLASLt), e4m3fn operands, bf16 "
-                       "output, no per-128-K scaling", "rotation_copies": copies,
+                       "output, no per-128-K scaling", "rotation_copies": r["rotation_copies"],
                        "timing": "eager"},
-            "forms": out}
+            "forms": r["forms"]}
+
+
+def vendor_decode(K: int, rotate: int) -> dict:
+    """The vendor reference on the decode shapes 64x2112x7168 and 64x32768x512 (see
+    vendor_gemm), graph-replayed like this library's decode step; bytes are the operand
+    and output bytes (no scales), GB/s against the same 8 TB/s."""
+    r = vendor_gemm(["dec2112", "dec32768"], K, rotate, True)
+    best = {n: min(v["forms"].values(), key=lambda d: d["avg_us"]) for n, v in r.items()}
+    total_bytes = sum(DECODE_BYTES.values())
+    step_us = sum(b["avg_us"] for b in best.values())
+    return {"metric": "vendor FP8 GEMM GB/s on the decode pair (reference point)",
+            "value": total_bytes / (step_us * 1e-6) / 1e9, "unit": "GB/s", "n_gpus": 1,
+            "steps": K, "higher_is_better": True, "dtype": "fp8", "data": "synthetic",
+            "config": {"workload": "torch._scaled_mm (hipBLASLt), e4m3fn operands, bf16 "
+                       "output, no per-128-K scaling; 64x2112x7168 + 64x32768x512",
+                       "timing": "graph"},
+            "gemms": r}
 
 
 def prefill_leg(K: int, rotate: int, graph: bool) -> dict:
