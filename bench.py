@@ -465,7 +465,8 @@ def main():
                          "time has passed, so that the GPU clocks have left their idle state "
                          "(0: exactly --warmup steps, e.g. under a profiler)")
     ap.add_argument("--workload", default="decode",
-                    choices=sorted(WORKLOADS) + ["hbm_ceiling", "vendor_prefill", "vendor_decode"])
+                    choices=sorted(WORKLOADS) + ["hbm_ceiling", "vendor_prefill", "vendor_decode",
+                                                 "overlap_probe"])
     ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
                     help="graph: the K launches of each GEMM are captured into a HIP graph "
                          "and replayed (no host launch gaps); eager: launched from Python")
@@ -524,6 +525,11 @@ def main():
         return
     if args.workload == "vendor_decode":
         print(json.dumps(vendor_decode(args.steps, rotate)), flush=True)
+        return
+    if args.workload == "overlap_probe":
+        print(json.dumps({"metric": "ns per iteration of the overlap probe (libdg_probe.so)",
+                          "unit": "ns", "n_gpus": 1, "higher_is_better": False,
+                          "data": "synthetic", "overlap": overlap_probe()}), flush=True)
         return
     names = WORKLOADS[args.workload]
     if args.gemm is not None:
@@ -689,6 +695,47 @@ def mfma_ceiling(iters: int = 2000, reps: int = 10):
     flops = blocks * 8 * 4 * iters * 2.0 * 32 * 32 * 64
     mhz = sampler.mean()
     return flops / (ms * 1e-3) / 1e12, (mhz / 1e3 if mhz else None)
+
+
+def overlap_probe(iters: int = 400, rounds: int = 5) -> dict:
+    """The overlap probe (libdg_probe.so): per iteration each of 8 waves per CU issues
+    six 1 KB global->LDS DMAs and eight FP8 32x32x64 MFMAs, as the compute-bound kernel
+    does per K-block; modes: MFMA alone, DMA alone, both independent, MFMAs fed from the
+    DMA'd LDS stages (fragments read an iteration ahead), and that plus a wait, a barrier
+    and the promotion FMAs per iteration. Operand regions of 4 MB (L2-resident) and
+    64 MB (streamed from MALL); modes interleaved over `rounds`, median ns per iteration."""
+    import ctypes
+    import torch
+    from fp8_block_scaled_dg_amd import build as dgb
+    lib = ctypes.CDLL(dgb.PROBE_LIB_PATH)
+    lib.dg_probe_overlap.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    blocks = 256
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda:0")
+    modes = {0: "mfma", 1: "dma", 2: "mfma+dma", 3: "mfma on lds fragments (read ahead)",
+             4: "+ wait, barrier, promotion"}
+    regions = {mb: torch.randint(0, 256, (mb << 20,), dtype=torch.uint8, device="cuda:0")
+               for mb in (4, 64)}
+    res = {}
+    for r in range(rounds):
+        for mb, buf in regions.items():
+            for m in modes:
+                def launch(i, m=m, buf=buf, mb=mb):
+                    rc = lib.dg_probe_overlap(m, buf.data_ptr(), mb << 20, iters, blocks,
+                                              777 + i, sink.data_ptr(),
+                                              torch.cuda.current_stream().cuda_stream)
+                    assert rc == 0, rc
+                if r == 0:
+                    launch(0)
+                    torch.cuda.synchronize()
+                ms = timed_launches(launch, 5, 0, graph=True)
+                res.setdefault((mb, m), []).append(ms * 1e6 / iters)
+    out = {}
+    for (mb, m), v in sorted(res.items()):
+        v = sorted(v)
+        out.setdefault(f"{mb}MB", {})[modes[m]] = v[len(v) // 2]
+    return out
 
 
 def vendor_gemm(names, K: int, rotate: int, graph: bool) -> dict:

@@ -9,7 +9,11 @@
 //    kernel's), on register operands of pseudo-random e4m3fn bytes, four independent
 //    accumulator chains per wave and two waves per SIMD: the rate the matrix units
 //    sustain on this chip when nothing else runs, at the clock its power limit allows
-//    for random data.
+//    for random data;
+//  - how operand movement overlaps with that instruction: per iteration each of 8
+//    waves issues six 1 KB global->LDS DMAs (48 KB per workgroup, the compute-bound
+//    kernel's bytes per K-block) and eight FP8 MFMAs (its MFMAs per wave and K-block),
+//    alone or together, and with the MFMA operands read from the DMA'd LDS stages.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -84,6 +88,141 @@ __global__ void __launch_bounds__(512) mfma_rate_kernel(int iters, uint32_t seed
   if (x == 1.2345f) sink[t] = x;  // keeps the chains; practically never stores
 }
 
+
+// ---- overlap probe. Region: a power-of-two byte range the workgroups walk in 48 KB
+// windows (so that its size decides whether the loads hit L2 or come from MALL/HBM);
+// three LDS stages of 48 KB; at most two iterations of DMAs in flight.
+constexpr int kOvlLoads = 6;                        // 1 KB DMAs per wave and iteration
+constexpr int kOvlStage = 8 * kOvlLoads * 1024;     // 48 KB per workgroup and iteration
+constexpr uint32_t kOvlMask = 0xF7F7F7F7u;          // clears the NaN codes 0x7F / 0xFF
+
+template <int n>
+__device__ __forceinline__ void ovl_wait_vm() {  // vmcnt = n, others untouched
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x3F << 8) | (7 << 4));
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Fragments of one iteration from LDS stage `stage`: eight 32-byte operands per lane.
+__device__ __forceinline__ void ovl_frags(const uint8_t* lds, int stage, uint32_t fo, v8i (&f)[8]) {
+  const uint8_t* st = lds + stage * kOvlStage + fo;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32x4 x = *(const u32x4*)(st + k * 2048);
+    const u32x4 y = *(const u32x4*)(st + k * 2048 + 16);
+    f[k] = v8i{(int)(x.x & kOvlMask), (int)(x.y & kOvlMask), (int)(x.z & kOvlMask),
+               (int)(x.w & kOvlMask), (int)(y.x & kOvlMask), (int)(y.y & kOvlMask),
+               (int)(y.z & kOvlMask), (int)(y.w & kOvlMask)};
+  }
+}
+
+// MODE 0: MFMAs on register operands; 1: DMAs only; 2: both, independent; 3: MFMAs on
+// fragments read from the stage DMA'd two iterations earlier, read one iteration ahead;
+// 4: MODE 3 plus a wait and workgroup barrier per iteration and 64 promotion FMAs
+// interleaved between the MFMA pairs (the compute-bound kernel's per-K-block work).
+template <int MODE>
+__global__ void __launch_bounds__(512) overlap_kernel(const uint8_t* src, uint32_t region_mask,
+                                                      int iters, uint32_t seed, float* sink) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  constexpr bool MF = MODE != 1, DMA = MODE != 0, LDSF = MODE >= 3, FULL = MODE == 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t t = blockIdx.x * 512u + tid;
+#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-DMA builtin exists in the device pass only
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(src), 0, (int)(region_mask + 1), 0x00020000);
+  const uint32_t base = (uint32_t)blockIdx.x * 0x9E3779B1u;
+#endif
+  const uint32_t fo = (uint32_t)(wave * 4096 + lane * 32) % (uint32_t)(kOvlStage - 8 * 2048);
+  v8i f[8], g[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[k][e] = g[k][e] = rnd_codes(seed ^ (t * 64u + k * 8 + e));
+  v16f p0 = {}, p1 = {}, p2 = {}, p3 = {}, acc[4] = {};
+  const float sc = 1.0f + (float)(seed & 7) * 0.125f;
+  if (LDSF) {
+    __syncthreads();
+    ovl_frags(lds, 0, fo, f);
+  }
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v8i(&cur)[8] = h == 0 ? f : g;
+      v8i(&nxt)[8] = h == 0 ? g : f;
+      const int i2 = it + h;
+#if defined(__HIP_DEVICE_COMPILE__)
+      if constexpr (DMA) {
+        const uint32_t woff = (base + (uint32_t)i2 * kOvlStage) & region_mask &
+                              ~(uint32_t)(kOvlStage - 1);
+        const int s = (i2 + 2) % 3;
+#pragma unroll
+        for (int q = 0; q < kOvlLoads; ++q) {
+          const uint32_t o = (uint32_t)(wave * kOvlLoads + q) * 1024u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(lds + s * kOvlStage + o), 16,
+              (woff + o + 16 * lane) & region_mask, 0, 0, 0);
+        }
+      }
+#endif
+      if constexpr (MF) {
+        const v16f z = {};
+        p0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur[0], cur[1], FULL ? z : p0, 0, 0, 0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur[2], cur[1], FULL ? z : p1, 0, 0, 0, 0, 0, 0);
+        if constexpr (FULL) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[2][e] = __builtin_fmaf(p2[e], sc, acc[2][e]);
+        }
+        p0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur[3], cur[4], p0, 0, 0, 0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur[5], cur[4], p1, 0, 0, 0, 0, 0, 0);
+        if constexpr (FULL) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[3][e] = __builtin_fmaf(p3[e], sc, acc[3][e]);
+          ovl_wait_vm<kOvlLoads>();
+          __builtin_amdgcn_s_barrier();
+        }
+        if constexpr (LDSF) ovl_frags(lds, (i2 + 1) % 3, fo, nxt);
+        p2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur[0], cur[6], FULL ? z : p2, 0, 0, 0, 0, 0, 0);
+        p3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur[2], cur[6], FULL ? z : p3, 0, 0, 0, 0, 0, 0);
+        if constexpr (FULL) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[0][e] = __builtin_fmaf(p0[e], sc, acc[0][e]);
+        }
+        p2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur[3], cur[7], p2, 0, 0, 0, 0, 0, 0);
+        p3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur[5], cur[7], p3, 0, 0, 0, 0, 0, 0);
+        if constexpr (FULL) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[1][e] = __builtin_fmaf(p1[e], sc, acc[1][e]);
+        }
+      }
+      if constexpr (DMA && !FULL) ovl_wait_vm<kOvlLoads>();
+    }
+  }
+  ovl_wait_vm<0>();
+  float x = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    x += p0[e] + p1[e] + p2[e] + p3[e] + acc[0][e] + acc[1][e] + acc[2][e] + acc[3][e];
+  uint32_t hsh = __float_as_uint(x);
+  if (DMA) {
+    __syncthreads();
+    hsh ^= (uint32_t)lds[(tid * 97) % (3 * kOvlStage)] * 0x01000193u;
+  }
+  if (hsh == 0x7A3C91E5u) sink[t] = x;  // keeps the work; practically never stores
+}
+
+template <int MODE>
+int overlap_launch(const void* src, uint32_t mask, int iters, int blocks, uint32_t seed,
+                   float* sink, hipStream_t s) {
+  static hipError_t attr = hipFuncSetAttribute((const void*)overlap_kernel<MODE>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               3 * kOvlStage);
+  if (attr != hipSuccess) return (int)attr;
+  hipLaunchKernelGGL(overlap_kernel<MODE>, dim3((unsigned)blocks), dim3(512), 3 * kOvlStage, s,
+                     (const uint8_t*)src, mask, iters, seed, sink);
+  return (int)hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,6 +253,29 @@ int dg_probe_mfma_rate(int32_t iters, int32_t blocks, uint32_t seed, float* sink
   hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(512), 0, (hipStream_t)stream,
                      iters, seed, sink);
   return (int)hipGetLastError();
+}
+
+// The overlap probe (see overlap_kernel): `mode` 0..4, `blocks` workgroups of 8 waves
+// (one per CU: each uses 144 KB of LDS), `iters` iterations (a positive even number).
+// src (device) holds region_bytes bytes, a power of two from 64 KB to 1 GB, 16-byte
+// aligned; sink (device) must hold blocks * 512 floats and is written only in the
+// improbable case that a checksum hits its marker value. 0 on success, else the HIP
+// error code.
+int dg_probe_overlap(int32_t mode, const void* src, int64_t region_bytes, int32_t iters,
+                     int32_t blocks, uint32_t seed, float* sink, void* stream) {
+  if (!src || !sink || blocks < 1 || iters < 2 || (iters & 1) || ((uintptr_t)src & 15) ||
+      region_bytes < (1 << 16) || region_bytes > (1 << 30) || (region_bytes & (region_bytes - 1)))
+    return (int)hipErrorInvalidValue;
+  const uint32_t mask = (uint32_t)(region_bytes - 1);
+  hipStream_t s = (hipStream_t)stream;
+  switch (mode) {
+    case 0: return overlap_launch<0>(src, mask, iters, blocks, seed, sink, s);
+    case 1: return overlap_launch<1>(src, mask, iters, blocks, seed, sink, s);
+    case 2: return overlap_launch<2>(src, mask, iters, blocks, seed, sink, s);
+    case 3: return overlap_launch<3>(src, mask, iters, blocks, seed, sink, s);
+    case 4: return overlap_launch<4>(src, mask, iters, blocks, seed, sink, s);
+    default: return (int)hipErrorInvalidValue;
+  }
 }
 
 // An empty kernel: the launch and completion cost alone.
